@@ -1,0 +1,132 @@
+"""Seeded synthetic attention inputs: the one module both sides draw from.
+
+This module holds no attention arithmetic: it only names workloads and draws
+their Q, K, V tensors from a seeded CPU generator.  The HIP path and the fp64
+oracle both take the bytes produced here.
+
+The shapes follow the prefill workloads of the page "A Thread-Register
+Decoupled GPU Execution Model for Efficient Tensor Computation" (evaluation
+set-up, "Workloads": Llama-family prefill attention with L_context = 4096 and
+d_head = 128, plus the grouped-query variant).  No dataset or trained weights
+are involved; the value distributions are stated per workload.
+
+Recipe (identical for every workload):
+  g = torch.Generator().manual_seed(seed)
+  Q, K, V drawn in that order, each as one [B, H, S, D] fp32 tensor (BHSD order),
+  normal draws are torch.randn(...) * sigma, uniform draws are torch.rand(...) * 2 - 1,
+  then cast to the storage dtype with round-to-nearest-even (torch .to()).
+"""
+from dataclasses import dataclass, field
+import math
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "bf16" | "fp16" | "fp32"
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    seed: int
+    q_dist: tuple = ("normal", 1.0)   # ("normal", sigma) or ("uniform", half_width)
+    k_dist: tuple = ("normal", 1.0)
+    v_dist: tuple = ("normal", 1.0)
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def visible_pairs(self) -> int:
+        """Number of (query, key) pairs inside the mask, over all heads."""
+        return visible_pairs(self.B, self.Hq, self.Sq, self.Sk, self.causal)
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs: 2*D for the score dot product plus 2*D for the
+        weighted sum of V, per visible (query, key) pair."""
+        return 4 * self.D * self.visible_pairs()
+
+    def min_hbm_bytes(self) -> int:
+        """Q, K, V read once, O and LSE written once."""
+        es = torch.tensor([], dtype=torch_dtype(self.dtype)).element_size()
+        q = self.B * self.Hq * self.Sq * self.D
+        kv = 2 * self.B * self.Hkv * self.Sk * self.D
+        return es * (2 * q + kv) + 4 * self.B * self.Hq * self.Sq
+
+
+def visible_pairs(B, Hq, Sq, Sk, causal) -> int:
+    if not causal:
+        return B * Hq * Sq * Sk
+    # query i sees keys 0 .. i + (Sk - Sq), clipped to [0, Sk]
+    off = Sk - Sq
+    tot = 0
+    # closed form over the three regimes of i
+    lo = max(0, -off)              # first row with at least one visible key
+    full = max(lo, min(Sq, Sk - off))  # rows i >= Sk - off see all Sk keys
+    # rows lo .. full-1 see i + off + 1 keys
+    n = full - lo
+    if n > 0:
+        a = lo + off + 1
+        tot += n * a + n * (n - 1) // 2
+    tot += (Sq - full) * Sk
+    return B * Hq * tot
+
+
+def torch_dtype(name: str):
+    return {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[name]
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("mha_fp32_b1_h2_s128_d64", "fp32", 1, 2, 2, 128, 128, 64, False, 1001,
+                 note="small fp32 case, non-causal"),
+        Workload("mha_bf16_b4_h16_s1024_d64", "bf16", 4, 16, 16, 1024, 1024, 64, False, 1002,
+                 note="non-causal, d_head 64"),
+        Workload("mha_causal_bf16_b2_h32_s4096_d128", "bf16", 2, 32, 32, 4096, 4096, 128, True,
+                 1003, note="Llama-style prefill, L_context 4096, d_head 128 (headline)"),
+        Workload("gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128", "bf16", 1, 32, 8, 8192, 8192, 128,
+                 True, 1004, v_dist=("uniform", 1.0),
+                 note="grouped-query, 4 query heads per key/value head"),
+        Workload("mha_causal_bf16_b1_h16_s16384_d128_peaky", "bf16", 1, 16, 16, 16384, 16384,
+                 128, True, 1005, q_dist=("normal", 2.0), k_dist=("normal", 2.0),
+                 note="long context; Q, K with sigma 2 make the softmax peaky"),
+    ]
+}
+
+# The workload the headline metric is quoted on (bf16, causal, S = 4096, D = 128).
+HEADLINE = "mha_causal_bf16_b2_h32_s4096_d128"
+# The order the five workloads are listed in (smallest first).
+ORDER = list(WORKLOADS)
+
+
+def _draw(g, shape, dist):
+    kind, p = dist
+    if kind == "normal":
+        return torch.randn(shape, generator=g, dtype=torch.float32) * p
+    if kind == "uniform":
+        return (torch.rand(shape, generator=g, dtype=torch.float32) * 2 - 1) * p
+    raise ValueError(kind)
+
+
+def make_inputs(w: Workload, seed=None):
+    """Draw (q, k, v) on the CPU in w's storage dtype; contiguous BHSD."""
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+    dt = torch_dtype(w.dtype)
+    q = _draw(g, (w.B, w.Hq, w.Sq, w.D), w.q_dist).to(dt)
+    k = _draw(g, (w.B, w.Hkv, w.Sk, w.D), w.k_dist).to(dt)
+    v = _draw(g, (w.B, w.Hkv, w.Sk, w.D), w.v_dist).to(dt)
+    return q, k, v
+
+
+def custom(dtype, B, Hq, Hkv, Sq, Sk, D, causal, seed, q_dist=("normal", 1.0),
+           k_dist=("normal", 1.0), v_dist=("normal", 1.0), name=None) -> Workload:
+    """A workload of arbitrary shape with the same recipe (for parity cases)."""
+    name = name or "custom_%s_b%d_hq%d_hkv%d_sq%d_sk%d_d%d_%s" % (
+        dtype, B, Hq, Hkv, Sq, Sk, D, "causal" if causal else "full")
+    return Workload(name, dtype, B, Hq, Hkv, Sq, Sk, D, causal, seed, q_dist, k_dist, v_dist)

@@ -1,0 +1,153 @@
+"""fp64 CPU oracle for the fused attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of
+`bench.py` may import this package.  The product path (the HIP library and its
+Python binding) never imports it, and this package imports nothing from the
+product.
+
+The arithmetic lives in `attn_oracle.c` (plain C, fp64, two-pass softmax per
+row); this module only marshals arrays into it.  What it computes: the
+multi-head scaled dot-product attention of Equ. 1 on the page "A
+Thread-Register Decoupled GPU Execution Model for Efficient Tensor Computation"
+(introduction), with the readings listed at the top of `attn_oracle.c`.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2, "fp64": 3}
+
+
+def _as_raw(x):
+    """Return (contiguous numpy array holding the raw storage bits, dtype name).
+
+    Accepts numpy arrays (float16/32/64) and CPU torch tensors (bfloat16,
+    float16, float32, float64).  bf16 has no numpy type, so its bits travel as
+    uint16 and the C side widens them exactly.
+    """
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    if torch is not None and isinstance(x, torch.Tensor):
+        x = x.detach().cpu().contiguous()
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).numpy().view(np.uint16), "bf16"
+        if x.dtype == torch.float16:
+            return x.view(torch.int16).numpy().view(np.uint16), "fp16"
+        if x.dtype == torch.float32:
+            return x.numpy(), "fp32"
+        if x.dtype == torch.float64:
+            return x.numpy(), "fp64"
+        raise TypeError("oracle: unsupported torch dtype %s" % x.dtype)
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        return x.view(np.uint16), "fp16"
+    if x.dtype == np.float32:
+        return x, "fp32"
+    if x.dtype == np.float64:
+        return x, "fp64"
+    raise TypeError("oracle: unsupported numpy dtype %s" % x.dtype)
+
+
+class OracleLib:
+    """ctypes view of one build of `attn_oracle.c` (the default build, or a
+    deliberately broken copy that the mutation tests compile on the CPU)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_attn_rows.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                         f64, i32, vp, i64, vp, vp, i32]
+        lib.oracle_attn_rows.restype = i32
+        lib.oracle_widen.argtypes = [vp, i32, i64, vp]
+        lib.oracle_widen.restype = i32
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = i32
+        self.lib = lib
+        self.path = path
+
+    def widen(self, x) -> np.ndarray:
+        """Exact fp64 copy of a bf16/fp16/fp32/fp64 array (same shape)."""
+        raw, name = _as_raw(x)
+        out = np.empty(raw.shape, dtype=np.float64)
+        rc = self.lib.oracle_widen(raw.ctypes.data, _DTYPE_CODE[name], raw.size,
+                                   out.ctypes.data)
+        if rc:
+            raise ValueError("oracle_widen failed (%d)" % rc)
+        return out
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+    def attn_fwd(self, q, k, v, causal=False, scale=None, rows=None, nthreads=0):
+        """fp64 attention forward.
+
+        q: [B, Hq, Sq, D]; k, v: [B, Hkv, Sk, D]; all three of one storage dtype.
+        rows: None for every query row, else an int array of flat row indices
+              r = (b * Hq + h) * Sq + i.
+        Returns (o, lse): with rows=None, o is [B, Hq, Sq, D] and lse [B, Hq, Sq];
+        otherwise o is [len(rows), D] and lse [len(rows)].  All float64.
+        """
+        qr, qn = _as_raw(q)
+        kr, kn = _as_raw(k)
+        vr, vn = _as_raw(v)
+        if not (qn == kn == vn):
+            raise TypeError("oracle: q, k, v must share one dtype")
+        if qr.ndim != 4 or kr.ndim != 4 or vr.ndim != 4:
+            raise ValueError("oracle: q, k, v must be 4-D [B, H, S, D]")
+        B, Hq, Sq, D = qr.shape
+        Bk, Hkv, Sk, Dk = kr.shape
+        if (Bk, Dk) != (B, D) or vr.shape != kr.shape:
+            raise ValueError("oracle: shape mismatch q%s k%s v%s"
+                             % (qr.shape, kr.shape, vr.shape))
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        total = B * Hq * Sq
+        if rows is None:
+            nrows, rows_ptr = total, None
+        else:
+            rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+            nrows, rows_ptr = rows_arr.size, rows_arr.ctypes.data
+        o = np.empty((nrows, D), dtype=np.float64)
+        lse = np.empty((nrows,), dtype=np.float64)
+        rc = self.lib.oracle_attn_rows(qr.ctypes.data, kr.ctypes.data, vr.ctypes.data,
+                                       _DTYPE_CODE[qn], B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                       int(bool(causal)), rows_ptr, nrows,
+                                       o.ctypes.data, lse.ctypes.data, int(nthreads))
+        if rc:
+            raise ValueError("oracle_attn_rows failed (%d)" % rc)
+        if rows is None:
+            return o.reshape(B, Hq, Sq, D), lse.reshape(B, Hq, Sq)
+        return o, lse
+
+
+_default = None
+
+
+def default() -> OracleLib:
+    """The oracle built from `attn_oracle.c` (rebuilt if the source is newer)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB) or (
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        _default = OracleLib(_build.LIB)
+    return _default
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, rows=None, nthreads=0):
+    return default().attn_fwd(q, k, v, causal=causal, scale=scale, rows=rows,
+                              nthreads=nthreads)
+
+
+def widen(x) -> np.ndarray:
+    return default().widen(x)
+
+
+def max_threads() -> int:
+    return default().max_threads()

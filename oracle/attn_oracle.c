@@ -1,0 +1,201 @@
+/*
+ * attn_oracle.c -- plain fp64 CPU oracle for the fused attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only the
+ * test-suite, the smoke check and the CPU-baseline leg of the benchmark load the
+ * library built from it.  It shares no code, header, table or helper with the
+ * HIP path, and the HIP path never calls it.
+ *
+ * What it computes.  The page "A Thread-Register Decoupled GPU Execution Model
+ * for Efficient Tensor Computation" (introduction) names multi-head attention,
+ * "Equ. 1", as the core of a transformer block and the FlashAttention series as
+ * its fused implementation.  The text of Equ. 1 did not survive extraction; it
+ * is read here as standard scaled dot-product attention applied per head:
+ *
+ *     s_ij  = scale * sum_d Q[i,d] * K[j,d]           for every visible key j
+ *     m_i   = max_j s_ij
+ *     l_i   = sum_j exp(s_ij - m_i)
+ *     O_i   = sum_j exp(s_ij - m_i) * V[j,:] / l_i
+ *     LSE_i = m_i + ln(l_i)
+ *
+ * FlashAttention reaches the same result (up to rounding order) with a tiled
+ * pass and an online softmax; the oracle does not tile, does not fuse and keeps
+ * the plain two-pass softmax per row, all in fp64.
+ *
+ * Readings where the pages are silent (each one listed in the design notes):
+ *   - layout: q, o are [B][Hq][Sq][D]; k, v are [B][Hkv][Sk][D]; lse is [B][Hq][Sq];
+ *     all contiguous, D fastest.
+ *   - grouped heads (the evaluation's GQA/MQA variants, "eight heads per group"):
+ *     query head h reads key/value head h / (Hq / Hkv), i.e. consecutive groups.
+ *   - causal mask with Sq != Sk: aligned bottom-right, key j is visible from query
+ *     i iff j <= i + (Sk - Sq); a query with no visible key gets O = 0, LSE = -inf.
+ *   - LSE is the natural logarithm of the sum of exponentials of the scaled scores.
+ *   - inputs arrive already rounded to their storage type (bf16, fp16, fp32 or
+ *     fp64) and are widened exactly to fp64 before any arithmetic.
+ *
+ * Parity status: every function here is pinned by the CPU tests (closed forms,
+ * invariants, 50-digit brute force on tiny inputs, an independent library
+ * routine); the pages print no attention values to pin against.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* storage-type codes accepted by the oracle (its own numbering) */
+enum { ORACLE_BF16 = 0, ORACLE_FP16 = 1, ORACLE_FP32 = 2, ORACLE_FP64 = 3 };
+
+/* Widen one bfloat16 bit pattern: bf16 is the top half of an IEEE binary32. */
+static double widen_bf16(uint16_t bits) {
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/* Widen one IEEE-754 binary16 bit pattern from its definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double widen_fp16(uint16_t bits) {
+    int sign = (bits >> 15) & 1;
+    int expo = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24);               /* subnormal: frac * 2^-14 * 2^-10 */
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(frac | 0x400), expo - 25); /* (1024 + frac) * 2^(e-15-10) */
+    return sign ? -mag : mag;
+}
+
+static double load_elem(const void* base, int dtype, size_t idx) {
+    switch (dtype) {
+    case ORACLE_BF16: return widen_bf16(((const uint16_t*)base)[idx]);
+    case ORACLE_FP16: return widen_fp16(((const uint16_t*)base)[idx]);
+    case ORACLE_FP32: return (double)((const float*)base)[idx];
+    default:          return ((const double*)base)[idx];
+    }
+}
+
+/* Widen n elements of a storage-typed array into fp64 (test helper). */
+int oracle_widen(const void* src, int dtype, int64_t n, double* dst) {
+    if (!src || !dst || n < 0 || dtype < ORACLE_BF16 || dtype > ORACLE_FP64) return 1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(src, dtype, (size_t)i);
+    return 0;
+}
+
+/* One query row of one head: scores, two-pass softmax, weighted sum of V. */
+static void one_row(const void* q, const void* k, const void* v, int dtype,
+                    int Hq, int Hkv, int Sq, int Sk, int D, double scale, int causal,
+                    int64_t row, double* qrow, double* s, double* o_out, double* lse_out) {
+    const int64_t i  = row % Sq;
+    const int64_t bh = row / Sq;
+    const int64_t h  = bh % Hq;
+    const int64_t b  = bh / Hq;
+    const int64_t kvh = h / (Hq / Hkv);
+
+    const size_t q_off  = (size_t)row * (size_t)D;
+    const size_t kv_off = ((size_t)b * (size_t)Hkv + (size_t)kvh) * (size_t)Sk * (size_t)D;
+
+    /* visible keys: 0 .. last (inclusive) */
+    int64_t last = Sk - 1;
+    if (causal) {
+        int64_t lim = i + ((int64_t)Sk - (int64_t)Sq);
+        if (lim < last) last = lim;
+    }
+    if (last < 0) {                      /* no visible key */
+        for (int d = 0; d < D; ++d) o_out[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+
+    for (int d = 0; d < D; ++d) qrow[d] = load_elem(q, dtype, q_off + (size_t)d);
+
+    /* pass 1: scaled scores and their maximum */
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= last; ++j) {
+        double dot = 0.0;
+        const size_t kr = kv_off + (size_t)j * (size_t)D;
+        for (int d = 0; d < D; ++d) dot += qrow[d] * load_elem(k, dtype, kr + (size_t)d);
+        s[j] = scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+
+    /* pass 2: exponentials relative to the maximum, their sum, and the V mix */
+    double l = 0.0;
+    for (int d = 0; d < D; ++d) o_out[d] = 0.0;
+    for (int64_t j = 0; j <= last; ++j) {
+        const double w = exp(s[j] - m);
+        l += w;
+        const size_t vr = kv_off + (size_t)j * (size_t)D;
+        for (int d = 0; d < D; ++d) o_out[d] += w * load_elem(v, dtype, vr + (size_t)d);
+    }
+    for (int d = 0; d < D; ++d) o_out[d] /= l;
+    *lse_out = m + log(l);
+}
+
+/*
+ * Attention forward for a list of query rows (or all rows when rows == NULL).
+ *   row index r = (b * Hq + h) * Sq + i
+ *   o   : nrows x D doubles, row-major, in the order of `rows`
+ *   lse : nrows doubles (may be NULL)
+ *   nthreads <= 0 uses the OpenMP default.
+ * Returns 0 on success, 1 on an invalid argument (nothing written).
+ */
+int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                     double scale, int causal,
+                     const int64_t* rows, int64_t nrows,
+                     double* o, double* lse, int nthreads) {
+    if (!q || !k || !v || !o) return 1;
+    if (dtype < ORACLE_BF16 || dtype > ORACLE_FP64) return 1;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1) return 1;
+    if (Hq % Hkv != 0) return 1;
+    const int64_t total = (int64_t)B * Hq * Sq;
+    if (rows == NULL && nrows != total) return 1;
+    if (nrows < 0) return 1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= total) return 1;
+
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+        double* s    = (double*)malloc(sizeof(double) * (size_t)Sk);
+        double  lse_dummy;
+        if (!qrow || !s) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t r = 0; r < nrows; ++r) {
+                const int64_t row = rows ? rows[r] : r;
+                one_row(q, k, v, dtype, Hq, Hkv, Sq, Sk, D, scale, causal, row, qrow, s,
+                        o + (size_t)r * (size_t)D, lse ? lse + r : &lse_dummy);
+            }
+        }
+        free(qrow);
+        free(s);
+    }
+    return bad ? 2 : 0;
+}
+
+/* Number of threads an OpenMP parallel region here would use. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,389 @@
+"""Pins for the fp64 oracle: facts fixed by the mathematics, not by the oracle.
+
+Every function takes an `OracleLib` and raises AssertionError when the oracle
+disagrees with the fact it checks.  `test_oracle_pins.py` runs them against the
+real oracle; `test_oracle_mutants.py` runs them against deliberately broken
+copies of the oracle (built on the CPU) and requires each copy to fail at least
+one pin.  Together they show the pins can see a dropped term, a wrong sign or
+index, or a transposed operand.
+
+What the oracle follows: the multi-head scaled dot-product attention of Equ. 1
+on the page "A Thread-Register Decoupled GPU Execution Model for Efficient
+Tensor Computation" (introduction); the readings for grouped heads and for the
+causal mask are stated in `oracle/attn_oracle.c`.
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_examples.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(rng, shape, sigma=1.0):
+    return rng.standard_normal(shape) * sigma
+
+
+# ----------------------------------------------------------------------------
+# 1. Brute force at 50 significant digits on tiny inputs.
+#    Visibility is written from positions: the Sq queries are the last Sq of the
+#    Sk positions, and a query sees every key at or before its own position.
+#    The softmax is taken without any max-subtraction (Decimal has the range),
+#    so the oracle's stabilised two-pass form is checked against the raw one.
+# ----------------------------------------------------------------------------
+def _brute_decimal(q, k, v, scale, causal):
+    getcontext().prec = 50
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    per_kv = Hq // Hkv
+    o = np.zeros((B, Hq, Sq, D))
+    lse = np.zeros((B, Hq, Sq))
+    dscale = Decimal(scale)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // per_kv
+            for i in range(Sq):
+                qpos = (Sk - Sq) + i
+                vis = [j for j in range(Sk) if (not causal) or j <= qpos]
+                if not vis:
+                    lse[b, h, i] = -math.inf
+                    continue
+                e = []
+                for j in vis:
+                    dot = sum(Decimal(q[b, h, i, d]) * Decimal(k[b, kh, j, d]) for d in range(D))
+                    e.append((dscale * dot).exp())
+                z = sum(e)
+                for d in range(D):
+                    num = sum(ej * Decimal(v[b, kh, j, d]) for ej, j in zip(e, vis))
+                    o[b, h, i, d] = float(num / z)
+                lse[b, h, i] = float(z.ln())
+    return o, lse
+
+
+BRUTE_SHAPES = [
+    # (B, Hq, Hkv, Sq, Sk, D, causal)
+    (1, 1, 1, 5, 5, 3, False),
+    (1, 1, 1, 5, 5, 3, True),
+    (2, 4, 2, 4, 7, 3, True),    # fewer queries than keys, grouped heads
+    (1, 2, 1, 7, 4, 2, True),    # more queries than keys: leading rows see nothing
+    (2, 3, 3, 3, 6, 4, False),
+    (1, 4, 1, 6, 6, 5, True),    # one key/value head for all query heads
+]
+
+
+def pin_bruteforce_decimal(orc):
+    for n, (B, Hq, Hkv, Sq, Sk, D, causal) in enumerate(BRUTE_SHAPES):
+        rng = _rng(100 + n)
+        q = _rand(rng, (B, Hq, Sq, D), 1.5)
+        k = _rand(rng, (B, Hkv, Sk, D), 1.5)
+        v = _rand(rng, (B, Hkv, Sk, D))
+        scale = 1.0 / math.sqrt(D) * (1.0 + 0.1 * n)
+        o, lse = orc.attn_fwd(q, k, v, causal=causal, scale=scale)
+        ob, lb = _brute_decimal(q, k, v, scale, causal)
+        assert np.allclose(o, ob, rtol=0, atol=1e-12), ("brute O", n, np.abs(o - ob).max())
+        fin = np.isfinite(lb)
+        assert np.array_equal(np.isfinite(lse), fin), ("brute LSE finiteness", n)
+        assert np.all(lse[~fin] == -math.inf), ("empty rows LSE", n)
+        assert np.allclose(lse[fin], lb[fin], rtol=0, atol=1e-12), ("brute LSE", n)
+
+
+# ----------------------------------------------------------------------------
+# 2. Hand-derived worked examples (tests/golden/hand_examples.json).
+# ----------------------------------------------------------------------------
+def pin_hand_examples(orc):
+    with open(GOLDEN) as f:
+        data = json.load(f)
+    for ex in data["examples"]:
+        B, Hq, Hkv, Sq, Sk, D = (ex[x] for x in ("B", "Hq", "Hkv", "Sq", "Sk", "D"))
+        q = np.array(ex["q"], dtype=np.float64).reshape(B, Hq, Sq, D)
+        k = np.array(ex["k"], dtype=np.float64).reshape(B, Hkv, Sk, D)
+        v = np.array(ex["v"], dtype=np.float64).reshape(B, Hkv, Sk, D)
+        o_ref = np.array(ex["o"], dtype=np.float64).reshape(B, Hq, Sq, D)
+        lse_ref = np.array([float(x) for x in ex["lse"]], dtype=np.float64).reshape(B, Hq, Sq)
+        o, lse = orc.attn_fwd(q, k, v, causal=ex["causal"], scale=ex["scale"])
+        assert np.allclose(o, o_ref, rtol=0, atol=1e-12), (ex["name"], o, o_ref)
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lse), fin), (ex["name"], lse, lse_ref)
+        assert np.all(lse[~fin] == -math.inf), (ex["name"], lse)
+        assert np.allclose(lse[fin], lse_ref[fin], rtol=0, atol=1e-12), (ex["name"], lse, lse_ref)
+
+
+# ----------------------------------------------------------------------------
+# 3. Closed forms on random inputs.
+# ----------------------------------------------------------------------------
+def pin_constant_values(orc):
+    """Softmax weights sum to one: V rows all equal c gives O = c exactly-ish."""
+    rng = _rng(7)
+    for causal in (False, True):
+        B, Hq, Hkv, S, D = 2, 4, 2, 37, 16
+        q = _rand(rng, (B, Hq, S, D), 2.0)
+        k = _rand(rng, (B, Hkv, S, D), 2.0)
+        c = _rand(rng, (B, Hkv, 1, D))
+        v = np.broadcast_to(c, (B, Hkv, S, D)).copy()
+        o, _ = orc.attn_fwd(q, k, v, causal=causal)
+        expect = np.repeat(c, Hq // Hkv, axis=1)[:, :, 0, :][:, :, None, :]
+        assert np.allclose(o, np.broadcast_to(expect, o.shape), rtol=0, atol=1e-13)
+        ones = np.ones_like(v)
+        o1, _ = orc.attn_fwd(q, k, ones, causal=causal)
+        assert np.allclose(o1, 1.0, rtol=0, atol=1e-14)
+
+
+def pin_uniform_attention(orc):
+    """Q = 0: every score is 0, so O_i is the plain mean of V over the visible
+    keys and LSE_i = ln(number of visible keys)."""
+    rng = _rng(8)
+    B, Hq, Hkv, Sq, Sk, D = 1, 2, 1, 9, 13, 6
+    q = np.zeros((B, Hq, Sq, D))
+    k = _rand(rng, (B, Hkv, Sk, D), 3.0)
+    v = _rand(rng, (B, Hkv, Sk, D))
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, causal=causal)
+        for i in range(Sq):
+            n = (i + Sk - Sq + 1) if causal else Sk
+            mean = v[0, 0, :n, :].mean(axis=0)
+            for h in range(Hq):
+                assert np.allclose(o[0, h, i], mean, rtol=0, atol=1e-13), (causal, i)
+                assert abs(lse[0, h, i] - math.log(n)) < 1e-13, (causal, i)
+
+
+def pin_causal_boundary_rows(orc):
+    """Causal with Sq = Sk: row 0 sees only key 0 (O_0 = V_0, LSE_0 = scale q0.k0);
+    the last row sees every key, so it equals the non-causal result."""
+    rng = _rng(9)
+    B, H, S, D = 2, 3, 23, 8
+    q = _rand(rng, (B, H, S, D), 2.0)
+    k = _rand(rng, (B, H, S, D), 2.0)
+    v = _rand(rng, (B, H, S, D))
+    scale = 0.3
+    oc, lc = orc.attn_fwd(q, k, v, causal=True, scale=scale)
+    on, ln_ = orc.attn_fwd(q, k, v, causal=False, scale=scale)
+    assert np.allclose(oc[:, :, 0], v[:, :, 0], rtol=0, atol=1e-14)
+    assert np.allclose(lc[:, :, 0], scale * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]),
+                       rtol=0, atol=1e-13)
+    assert np.allclose(oc[:, :, -1], on[:, :, -1], rtol=0, atol=1e-13)
+    assert np.allclose(lc[:, :, -1], ln_[:, :, -1], rtol=0, atol=1e-13)
+    # row 1 sees exactly keys 0 and 1: a two-term softmax written out
+    s0 = scale * np.einsum("bhd,bhd->bh", q[:, :, 1], k[:, :, 0])
+    s1 = scale * np.einsum("bhd,bhd->bh", q[:, :, 1], k[:, :, 1])
+    w1 = 1.0 / (1.0 + np.exp(s0 - s1))
+    o1 = (1 - w1)[..., None] * v[:, :, 0] + w1[..., None] * v[:, :, 1]
+    assert np.allclose(oc[:, :, 1], o1, rtol=0, atol=1e-13)
+
+
+def pin_empty_rows(orc):
+    """Causal with Sq > Sk: the first Sq - Sk rows see no key: O = 0, LSE = -inf;
+    the next row sees key 0 only."""
+    rng = _rng(10)
+    B, H, Sq, Sk, D = 1, 2, 11, 4, 5
+    q = _rand(rng, (B, H, Sq, D))
+    k = _rand(rng, (B, H, Sk, D))
+    v = _rand(rng, (B, H, Sk, D))
+    o, lse = orc.attn_fwd(q, k, v, causal=True)
+    e = Sq - Sk
+    assert np.all(o[:, :, :e] == 0.0)
+    assert np.all(lse[:, :, :e] == -math.inf)
+    assert np.all(np.isfinite(lse[:, :, e:]))
+    assert np.allclose(o[:, :, e], v[:, :, 0], rtol=0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# 4. Invariants.
+# ----------------------------------------------------------------------------
+def pin_shift_invariance(orc):
+    """K' = K + 1 u^T adds scale*(q.u) to every score of a row: O is unchanged
+    and LSE shifts by scale*(q.u)."""
+    rng = _rng(11)
+    B, Hq, Hkv, Sq, Sk, D = 1, 4, 2, 10, 14, 7
+    q = _rand(rng, (B, Hq, Sq, D))
+    k = _rand(rng, (B, Hkv, Sk, D))
+    v = _rand(rng, (B, Hkv, Sk, D))
+    u = _rand(rng, (D,))
+    scale = 0.4
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, causal=causal, scale=scale)
+        o2, lse2 = orc.attn_fwd(q, k + u, v, causal=causal, scale=scale)
+        assert np.allclose(o2, o, rtol=0, atol=1e-12)
+        assert np.allclose(lse2, lse + scale * (q @ u), rtol=0, atol=1e-12)
+
+
+def pin_permutation(orc):
+    """Non-causal: permuting the key/value rows together leaves O and LSE
+    unchanged; permuting the query rows permutes O and LSE."""
+    rng = _rng(12)
+    B, Hq, Hkv, Sq, Sk, D = 2, 2, 1, 8, 12, 6
+    q = _rand(rng, (B, Hq, Sq, D))
+    k = _rand(rng, (B, Hkv, Sk, D))
+    v = _rand(rng, (B, Hkv, Sk, D))
+    o, lse = orc.attn_fwd(q, k, v)
+    pk = rng.permutation(Sk)
+    o2, lse2 = orc.attn_fwd(q, k[:, :, pk], v[:, :, pk])
+    assert np.allclose(o2, o, rtol=0, atol=1e-13)
+    assert np.allclose(lse2, lse, rtol=0, atol=1e-13)
+    pq = rng.permutation(Sq)
+    o3, lse3 = orc.attn_fwd(q[:, :, pq], k, v)
+    assert np.allclose(o3, o[:, :, pq], rtol=0, atol=1e-13)
+    assert np.allclose(lse3, lse[:, :, pq], rtol=0, atol=1e-13)
+
+
+def pin_scale_folding(orc):
+    """attn(Q, scale = s) equals attn(s Q, scale = 1); s a power of two keeps
+    s Q exact."""
+    rng = _rng(13)
+    B, H, S, D = 1, 2, 17, 8
+    q = _rand(rng, (B, H, S, D))
+    k = _rand(rng, (B, H, S, D))
+    v = _rand(rng, (B, H, S, D))
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, causal=causal, scale=0.25)
+        o2, lse2 = orc.attn_fwd(q * 0.25, k, v, causal=causal, scale=1.0)
+        assert np.allclose(o, o2, rtol=0, atol=1e-14)
+        assert np.allclose(lse, lse2, rtol=0, atol=1e-14)
+        o3, _ = orc.attn_fwd(q, k, v, causal=causal, scale=0.5)
+        assert not np.allclose(o, o3, rtol=0, atol=1e-6)
+
+
+def pin_grouped_heads(orc):
+    """Grouped heads equal plain multi-head attention on K/V heads repeated
+    Hq/Hkv times consecutively (the consecutive-group reading)."""
+    rng = _rng(14)
+    B, Hq, Hkv, S, D = 2, 6, 2, 11, 4
+    q = _rand(rng, (B, Hq, S, D))
+    k = _rand(rng, (B, Hkv, S, D))
+    v = _rand(rng, (B, Hkv, S, D))
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, causal=causal)
+        kr = np.repeat(k, Hq // Hkv, axis=1)
+        vr = np.repeat(v, Hq // Hkv, axis=1)
+        o2, lse2 = orc.attn_fwd(q, kr, vr, causal=causal)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+        # and the repetition really matters: head 0 differs from head Hq-1's source
+        o3, _ = orc.attn_fwd(q, k[:, ::-1].copy(), v[:, ::-1].copy(), causal=causal)
+        assert not np.allclose(o3, o, atol=1e-6)
+
+
+def pin_peaky_limit(orc):
+    """K_j = alpha * Q_i with alpha large makes key j dominate row i: O_i -> V_j
+    (one-hot softmax) and LSE_i -> alpha*scale*|q_i|^2."""
+    rng = _rng(15)
+    B, H, S, D = 1, 1, 6, 4
+    q = _rand(rng, (B, H, S, D))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = _rand(rng, (B, H, S, D)) * 0.01
+    perm = [3, 0, 5, 1, 4, 2]
+    alpha = 2000.0
+    for i, j in enumerate(perm):
+        k[0, 0, j] = alpha * q[0, 0, i]
+    v = _rand(rng, (B, H, S, D))
+    o, lse = orc.attn_fwd(q, k, v, scale=1.0)
+    for i, j in enumerate(perm):
+        assert np.allclose(o[0, 0, i], v[0, 0, j], rtol=0, atol=1e-12), (i, j)
+        assert abs(lse[0, 0, i] - alpha) < 1e-9, (i, lse[0, 0, i])
+
+
+# ----------------------------------------------------------------------------
+# 5. Storage types: the oracle's exact widening of bf16 / fp16 / fp32 inputs
+#    agrees with torch's own conversions, including fp16 subnormals, the largest
+#    finite values and signed zeros.
+# ----------------------------------------------------------------------------
+def pin_storage_widening(orc):
+    g = torch.Generator().manual_seed(16)
+    x = torch.randn(4096, generator=g) * 30
+    specials = torch.tensor([0.0, -0.0, 1.0, -1.0, 65504.0, -65504.0, 6.1e-5, 5.96e-8,
+                             -5.96e-8, 3.0e-6, 1e-7, 3.3895e38, 1.2e-38, 9.2e-41])
+    for dt in (torch.bfloat16, torch.float16, torch.float32):
+        y = torch.cat([x, specials]).to(dt)
+        w = orc.widen(y)
+        ref = y.to(torch.float64).numpy()
+        assert np.array_equal(np.signbit(w), np.signbit(ref)), dt
+        assert np.array_equal(w, ref), dt
+    # and through the attention path: bf16 inputs give the fp64 result of their
+    # widened values
+    q = (torch.randn(1, 2, 9, 8, generator=g)).to(torch.bfloat16)
+    k = (torch.randn(1, 1, 12, 8, generator=g)).to(torch.bfloat16)
+    v = (torch.randn(1, 1, 12, 8, generator=g)).to(torch.bfloat16)
+    o, lse = orc.attn_fwd(q, k, v, causal=True)
+    o2, lse2 = orc.attn_fwd(q.double(), k.double(), v.double(), causal=True)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    qh, kh, vh = (t.to(torch.float16) for t in (q, k, v))
+    o3, _ = orc.attn_fwd(qh, kh, vh, causal=True)
+    o4, _ = orc.attn_fwd(qh.double(), kh.double(), vh.double(), causal=True)
+    assert np.array_equal(o3, o4)
+
+
+# ----------------------------------------------------------------------------
+# 6. An independent library routine: torch's CPU scaled_dot_product_attention
+#    (math path) in fp64, with the bottom-right causal mask given explicitly.
+# ----------------------------------------------------------------------------
+SDPA_SHAPES = [
+    # (B, Hq, Hkv, Sq, Sk, D, causal)
+    (1, 2, 2, 128, 128, 64, False),
+    (2, 4, 1, 96, 160, 32, True),
+    (1, 8, 2, 200, 200, 128, True),
+    (1, 3, 3, 150, 70, 16, True),
+]
+
+
+def pin_torch_sdpa(orc):
+    import torch.nn.functional as F
+    g = torch.Generator().manual_seed(17)
+    for (B, Hq, Hkv, Sq, Sk, D, causal) in SDPA_SHAPES:
+        q = torch.randn(B, Hq, Sq, D, generator=g, dtype=torch.float64) * 1.5
+        k = torch.randn(B, Hkv, Sk, D, generator=g, dtype=torch.float64) * 1.5
+        v = torch.randn(B, Hkv, Sk, D, generator=g, dtype=torch.float64)
+        scale = 1.0 / math.sqrt(D)
+        mask = None
+        if causal:
+            mask = torch.ones(Sq, Sk, dtype=torch.bool).tril(diagonal=Sk - Sq)
+        ref = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale,
+                                             enable_gqa=(Hq != Hkv))
+        scores = (q @ torch.repeat_interleave(k, Hq // Hkv, dim=1).transpose(-1, -2)) * scale
+        if mask is not None:
+            scores = scores.masked_fill(~mask, -math.inf)
+        lse_ref = torch.logsumexp(scores, dim=-1)
+        o, lse = orc.attn_fwd(q, k, v, causal=causal, scale=scale)
+        live = torch.isfinite(lse_ref).numpy()
+        assert np.allclose(o[live], ref.numpy()[live], rtol=0, atol=1e-12), (B, Hq, Sq, Sk)
+        assert np.allclose(lse[live], lse_ref.numpy()[live], rtol=0, atol=1e-12)
+        assert np.all(o[~live] == 0.0) and np.all(lse[~live] == -math.inf)
+
+
+# ----------------------------------------------------------------------------
+# 7. Row selection: computing a list of rows one by one gives the same values
+#    as the full pass (the full-size GPU tests rely on it).
+# ----------------------------------------------------------------------------
+def pin_row_subset(orc):
+    rng = _rng(18)
+    B, Hq, Hkv, Sq, Sk, D = 2, 4, 2, 33, 41, 8
+    q = _rand(rng, (B, Hq, Sq, D))
+    k = _rand(rng, (B, Hkv, Sk, D))
+    v = _rand(rng, (B, Hkv, Sk, D))
+    o, lse = orc.attn_fwd(q, k, v, causal=True)
+    rows = rng.integers(0, B * Hq * Sq, size=50)
+    o_r, lse_r = orc.attn_fwd(q, k, v, causal=True, rows=rows)
+    assert np.array_equal(o_r, o.reshape(-1, D)[rows])
+    assert np.array_equal(lse_r, lse.reshape(-1)[rows])
+
+
+ALL_PINS = [
+    pin_bruteforce_decimal,
+    pin_hand_examples,
+    pin_constant_values,
+    pin_uniform_attention,
+    pin_causal_boundary_rows,
+    pin_empty_rows,
+    pin_shift_invariance,
+    pin_permutation,
+    pin_scale_folding,
+    pin_grouped_heads,
+    pin_peaky_limit,
+    pin_storage_widening,
+    pin_torch_sdpa,
+    pin_row_subset,
+]

@@ -1,0 +1,58 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies `oracle/attn_oracle.c`, plants one plausible mistake by a
+textual substitution, compiles the copy with gcc into a temporary directory and
+runs every pin against it.  A case passes when at least one pin fails; a pin
+set that cannot see the mistake would make this test fail.  The real oracle is
+never modified.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from oracle_pins import ALL_PINS
+
+MUTANTS = [
+    ("drop_scale", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("max_sign", "exp(s[j] - m)", "exp(m - s[j])"),
+    ("no_max_in_lse", "*lse_out = m + log(l);", "*lse_out = log(l);"),
+    ("no_normalisation", "o_out[d] /= l;", "o_out[d] /= 1.0;"),
+    ("causal_off_by_one", "int64_t lim = i + ((int64_t)Sk - (int64_t)Sq);",
+     "int64_t lim = i + ((int64_t)Sk - (int64_t)Sq) - 1;"),
+    ("causal_top_left", "int64_t lim = i + ((int64_t)Sk - (int64_t)Sq);", "int64_t lim = i;"),
+    ("grouped_heads_interleaved", "const int64_t kvh = h / (Hq / Hkv);",
+     "const int64_t kvh = h % Hkv;"),
+    ("scores_from_v", "qrow[d] * load_elem(k, dtype, kr", "qrow[d] * load_elem(v, dtype, kr"),
+    ("values_from_k", "w * load_elem(v, dtype, vr", "w * load_elem(k, dtype, vr"),
+    ("kv_stride_uses_sq", "(size_t)kvh) * (size_t)Sk * (size_t)D",
+     "(size_t)kvh) * (size_t)Sq * (size_t)D"),
+    ("empty_row_lse_zero", "*lse_out = -INFINITY;", "*lse_out = 0.0;"),
+    ("fp16_bias", "expo - 25", "expo - 24"),
+    ("fp16_subnormal", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    ("bf16_shift", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    ("last_key_dropped", "for (int64_t j = 0; j <= last; ++j) {\n        const double w",
+     "for (int64_t j = 0; j < last; ++j) {\n        const double w"),
+    ("exp_weight_unused_in_sum", "l += w;", "l += 1.0;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, "mutation pattern %r must occur exactly once" % name
+    mutated = tmp_path / ("attn_oracle_%s.c" % name)
+    mutated.write_text(src.replace(old, new))
+    lib = obuild.build(str(mutated), str(tmp_path / ("lib_%s.so" % name)))
+    orc = oracle.OracleLib(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except (ValueError, FloatingPointError, OverflowError):
+            failed.append(pin.__name__)
+    assert failed, "no pin caught the planted mistake %r" % name
