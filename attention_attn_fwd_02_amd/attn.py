@@ -1,0 +1,95 @@
+"""Thin Python binding of the C-ABI library `libattn_fwd.so` (include/attn_fwd.h).
+
+Argument marshalling only: every step of the attention forward runs in the HIP
+kernels behind `attn_fwd`.  PyTorch supplies device memory and the stream.  If
+the library is missing this module raises; there is no fallback path.
+"""
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn_fwd.so")
+
+# attn_dtype_t
+ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
+# attn_status_t
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__("attn_fwd failed: %s (%d)" % (attn_status_str(status), status))
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libattn_fwd.so is not built (%s); run "
+                           "`python -m attention_attn_fwd_02_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_status_str.argtypes = [i32]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, stream) -> int:
+    """The C entry point with raw integer pointers; returns the status code."""
+    return load_library().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                   int(causal), int(dtype), stream)
+
+
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def _dtype_code(t):
+    import torch
+    return {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16, torch.float32: ATTN_FP32}[t]
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True, stream=None):
+    """Attention forward on torch device tensors.
+
+    q: [B, Hq, Sq, D], k and v: [B, Hkv, Sk, D] (contiguous, one dtype: bf16,
+    fp16 or fp32).  Returns (o, lse) with o like q and lse [B, Hq, Sq] fp32 (None
+    when want_lse is False).  `out` / `lse` may be passed to reuse buffers.  The
+    call is asynchronous on `stream` (default: torch's current stream).
+    """
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch: q%s k%s v%s" % (tuple(q.shape), tuple(k.shape),
+                                                          tuple(v.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                  lse.data_ptr() if want_lse else None,
+                  B, Hq, Hkv, Sq, Sk, D, scale, causal, _dtype_code(q.dtype),
+                  stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, (lse if want_lse else None)

@@ -1,0 +1,50 @@
+"""Build the HIP library `libattn_fwd.so` (gfx950) in-tree with hipcc.
+
+    python -m attention_attn_fwd_02_amd.build          # build the library
+    python -m attention_attn_fwd_02_amd.build --asm D  # also write the device assembly to D/
+"""
+import argparse
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libattn_fwd.so")
+SOURCES = [os.path.join(CSRC, "attn_fwd_kernels.hip"), os.path.join(CSRC, "attn_fwd_api.cpp")]
+ARCH = "gfx950"
+
+# Packed fp32 VALU forms are kept out of the generated code (feature switched off).
+COMMON = ["-O3", "-std=c++17", "--offload-arch=" + ARCH,
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I" + INCLUDE, "-I" + CSRC, "-Wno-unused-command-line-argument"]
+
+
+def build(out: str = LIB, verbose: bool = False) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", *COMMON, "-fPIC", "-shared", *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def dump_asm(outdir: str) -> str:
+    """Device assembly of the kernels (for register / LDS / instruction-mix review)."""
+    os.makedirs(outdir, exist_ok=True)
+    out = os.path.join(outdir, "attn_fwd_kernels-%s.s" % ARCH)
+    cmd = ["hipcc", *COMMON, "-S", "--cuda-device-only", SOURCES[0], "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", default=None, help="also write device assembly into this folder")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args()
+    print(build(verbose=a.verbose))
+    if a.asm:
+        print(dump_asm(a.asm))

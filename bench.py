@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one `attn_fwd` call over the whole workload (default: bf16, causal,
+B = 2, H = 32, S = 4096, D = 128) with Q, K, V already resident in HBM.  After W
+untimed steps, exactly K steps are timed between two device synchronisations.
+One JSON line goes to stdout; progress goes to stderr.
+
+The line carries:
+  value / ms_per_step   whole-job TFLOP/s (4*D FLOPs per visible query-key pair)
+  roofline              the attention kernel against the dense bf16 MFMA peak, its
+                        average duration measured with HIP events on the launch stream;
+                        `traffic` is the HBM bytes per launch from the committed
+                        counter summary when it matches the current kernel source
+  cpu_baseline          the fp64 CPU oracle timed on a bounded sample of the same
+                        workload on this host (a reported baseline, not a target)
+
+`--copy-mib N` instead runs N-MiB device copies (the calibration kernel for the
+FETCH_SIZE / WRITE_SIZE counters).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+KERNEL_SRC = os.path.join(ROOT, "attention_attn_fwd_02_amd", "csrc", "attn_fwd_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # dense MFMA peaks, MI355X
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from profiles/attn_fwd_traffic_<workload>.txt, or None
+    when the summary is absent or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, "attn_fwd_traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int, steps: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copied %d MiB x %d" % (mib, steps))
+
+
+def cpu_baseline(w, q, k, v, target_s: float):
+    """Time the oracle (as it stands) on random query rows of the workload."""
+    import numpy as np
+    import oracle
+    from attention_attn_fwd_02_amd import workloads as W
+    total = w.B * w.Hq * w.Sq
+    rng = np.random.default_rng(12345)
+    off = w.Sk - w.Sq
+
+    def pairs(rows):
+        i = rows % w.Sq
+        if not w.causal:
+            return int(len(rows) * w.Sk)
+        return int(np.clip(i + off + 1, 0, w.Sk).sum())
+
+    probe = rng.integers(0, total, size=16)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, rows=probe)
+    t_probe = time.perf_counter() - t0
+    rate = pairs(probe) / max(t_probe, 1e-6)                 # pairs per second
+    mean_pairs = W.visible_pairs(w.B, w.Hq, w.Sq, w.Sk, w.causal) / total
+    n = int(max(16, min(total, target_s * rate / max(mean_pairs, 1.0))))
+    rows = rng.integers(0, total, size=n)
+    log("cpu baseline: oracle on %d rows (~%.0f s)" % (n, n * mean_pairs / rate))
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * pairs(rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d uniformly drawn query rows (seed 12345) of the %d rows, each over all "
+                      "its visible keys; fp64; %.1f s; FLOPs = 4*D per visible pair"
+                      % (n, total, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the attention forward shards over (batch, head) with no exchange, "
+              "so N GPUs would each run this one-GPU workload on their share)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, max(1, args.steps))
+        return
+
+    from attention_attn_fwd_02_amd import fwd, load_library
+    from attention_attn_fwd_02_amd import workloads as W
+    load_library()
+    name = args.workload or W.HEADLINE
+    w = W.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log("device: %s, %d CUs; workload %s" % (props.name, props.multi_processor_count, name))
+
+    q, k, v = W.make_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    flops = w.flops()
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log("timed %d steps: %.3f ms/step wall, %.3f ms/launch (events), %.1f TFLOP/s"
+        % (args.steps, wall_ms, kern_ms, achieved))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        log("cpu baseline: %.4g TFLOP/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    line = {
+        "metric": "attention fwd TFLOP/s (bf16, causal S=4096 D=128) + % of MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
+                   "Sk": w.Sk, "D": w.D, "causal": w.causal, "seed": w.seed,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": committed_traffic(name),
+                     "kernel_ms_per_launch": round(kern_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,95 @@
+/*
+ * attn_fwd.h -- C ABI of the fused attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  The page "A Thread-Register Decoupled GPU Execution Model for
+ * Efficient Tensor Computation" (introduction) names multi-head attention,
+ * Equ. 1, as the core of the transformer block and the FlashAttention series as
+ * its fused, tiled implementation; its evaluation ("Workloads", Tbl. III) runs
+ * the prefill attention of Llama-family models with L_context = 4096 and
+ * d_head = 128, and the grouped-query (GQA) and multi-query (MQA) variants.  The
+ * formula of Equ. 1 is not in the extracted text; it is read as scaled
+ * dot-product attention per head:
+ *
+ *     O[b,h,i,:] = sum_j softmax_j( scale * Q[b,h,i,:] . K[b,g(h),j,:] ) * V[b,g(h),j,:]
+ *     LSE[b,h,i] = ln sum_j exp( scale * Q[b,h,i,:] . K[b,g(h),j,:] )
+ *
+ * over the visible keys j, where g(h) = h / (Hq / Hkv) (consecutive groups of
+ * query heads share one key/value head; Hkv = Hq is plain multi-head attention,
+ * Hkv = 1 is multi-query attention) and, with causal != 0, key j is visible from
+ * query i iff j <= i + (Sk - Sq) (the mask is aligned to the bottom-right corner,
+ * so the last query sees every key).  A query that sees no key gets O = 0 and
+ * LSE = -inf.
+ *
+ * Numerics: scores, the running softmax statistics and O accumulate in fp32;
+ * for 16-bit inputs the softmax weights are rounded to the input type (round to
+ * nearest even) before they multiply V, and O is rounded once to the input type.
+ * fp32 inputs use fp32 products throughout.  Non-finite inputs propagate; they
+ * are not checked.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+typedef enum {
+    ATTN_BF16 = 0,   /* bfloat16 */
+    ATTN_FP16 = 1,   /* IEEE binary16 */
+    ATTN_FP32 = 2    /* IEEE binary32 */
+} attn_dtype_t;
+
+/* Return codes.  Every code is returned synchronously; the library never
+ * aborts, prints or exits. */
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,   /* a null or misaligned pointer, a size < 1, Hq % Hkv != 0,
+                                   a non-finite scale, an unknown dtype, or sizes whose
+                                   element counts overflow 64-bit offsets */
+    ATTN_ERR_UNSUPPORTED = 2,   /* a head dimension D other than 64 or 128, or a grid too
+                                   large for one launch */
+    ATTN_ERR_LAUNCH = 3         /* the HIP runtime refused the kernel launch */
+} attn_status_t;
+
+/*
+ * attn_fwd -- enqueue one fused attention forward on `stream`.
+ *
+ * Arguments (all pointers are device pointers, owned by the caller):
+ *   q      [B][Hq][Sq][D]   input, element type `dtype`, 16-byte aligned
+ *   k      [B][Hkv][Sk][D]  input, element type `dtype`, 16-byte aligned
+ *   v      [B][Hkv][Sk][D]  input, element type `dtype`, 16-byte aligned
+ *   o      [B][Hq][Sq][D]   output, element type `dtype`, 16-byte aligned; every
+ *                           element is written
+ *   lse    [B][Hq][Sq]      output, fp32, natural log, 4-byte aligned; may be NULL,
+ *                           in which case no log-sum-exp is written
+ *   B, Hq, Hkv, Sq, Sk      sizes, each >= 1; Hq must be a multiple of Hkv
+ *   D                       head dimension: 64 or 128
+ *   scale                   any finite value (1/sqrt(D) is the usual choice)
+ *   causal                  0: every key is visible; otherwise the bottom-right
+ *                           causal mask described above
+ *   dtype                   an attn_dtype_t
+ *   stream                  HIP stream to enqueue on (NULL: the default stream)
+ *
+ * All tensors are contiguous with D fastest.  q/o and k/v may not overlap o or
+ * lse.  The library allocates no memory and keeps no state between calls.  The
+ * call validates its arguments on the host before touching the device, enqueues
+ * one kernel and returns without synchronising: results are ready when `stream`
+ * reaches that point.  On any error nothing is enqueued and no output is
+ * written.  Results are deterministic: the same inputs give bitwise-identical
+ * outputs on every call.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D,
+             float scale, int causal, int dtype, hipStream_t stream);
+
+/* Static, human-readable name of a return code ("unknown status" otherwise). */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,82 @@
+"""Shared pieces of the GPU tests: run the HIP path, compare with the oracle."""
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from attention_attn_fwd_02_amd import fwd
+from attention_attn_fwd_02_amd import workloads as W
+
+# Tolerances on max |GPU - oracle| over every compared element.  The 16-bit and
+# fp32 bounds on O and the LSE bound are the stated targets; fp16 (3 more mantissa
+# bits than bf16) is held to the bf16 bound.
+TOL_O = {"bf16": 2e-2, "fp16": 2e-2, "fp32": 1e-4}
+TOL_LSE = 1e-3
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_gpu(q, k, v, causal, scale=None, want_lse=True, stream=None):
+    """Copy to cuda:0, run the HIP path into NaN-poisoned outputs, copy back."""
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = None
+    if want_lse:
+        lse = torch.full(qd.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    fwd(qd, kd, vd, causal=causal, scale=scale, out=o, lse=lse, want_lse=want_lse,
+        stream=stream)
+    torch.cuda.synchronize()
+    return o.cpu(), (lse.cpu() if want_lse else None)
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, tag=""):
+    """Element-wise comparison; returns (max O error, max LSE error)."""
+    og = o_gpu.to(torch.float64).numpy().reshape(o_ref.shape)
+    assert not np.isnan(og).any(), "%s: NaN in O (unwritten or invalid)" % tag
+    err_o = float(np.abs(og - o_ref).max()) if og.size else 0.0
+    assert err_o <= TOL_O[dtype], "%s: max |dO| = %.3g > %.3g" % (tag, err_o, TOL_O[dtype])
+    err_l = 0.0
+    if lse_gpu is not None:
+        lg = lse_gpu.to(torch.float64).numpy().reshape(lse_ref.shape)
+        assert not np.isnan(lg).any(), "%s: NaN in LSE" % tag
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lg), fin), "%s: LSE finiteness differs" % tag
+        assert np.all(lg[~fin] == -math.inf), "%s: empty rows must give -inf" % tag
+        if fin.any():
+            err_l = float(np.abs(lg[fin] - lse_ref[fin]).max())
+        assert err_l <= TOL_LSE, "%s: max |dLSE| = %.3g > %.3g" % (tag, err_l, TOL_LSE)
+    return err_o, err_l
+
+
+def check_full(w: W.Workload, scale=None, want_lse=True):
+    """Whole-output parity for a workload the oracle finishes in seconds."""
+    say("case", w.name, "scale", scale)
+    q, k, v = W.make_inputs(w)
+    sc = w.scale if scale is None else scale
+    o, lse = run_gpu(q, k, v, w.causal, scale=sc, want_lse=want_lse)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=w.causal, scale=sc)
+    e = compare(o, lse, o_ref, lse_ref if want_lse else None, w.dtype, w.name)
+    say("  max|dO| %.3g  max|dLSE| %.3g" % e)
+    return e
+
+
+def sample_rows(w: W.Workload, n_random: int, seed: int):
+    """Rows r = (b*Hq + h)*Sq + i to check at full size: random rows plus the
+    first and last query of every 256- and 128-query tile boundary of a few heads,
+    and the first and last rows of the problem."""
+    rng = np.random.default_rng(seed)
+    total = w.B * w.Hq * w.Sq
+    rows = set(rng.integers(0, total, size=n_random).tolist())
+    heads = rng.integers(0, w.B * w.Hq, size=3).tolist() + [0, w.B * w.Hq - 1]
+    for bh in heads:
+        for t in range(0, w.Sq, 256):
+            for i in (t, t + 1, t + 63, t + 64, t + 127, t + 128, t + 255):
+                if i < w.Sq:
+                    rows.add(bh * w.Sq + i)
+        rows.add(bh * w.Sq + w.Sq - 1)
+    return np.array(sorted(rows), dtype=np.int64)

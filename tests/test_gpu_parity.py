@@ -1,0 +1,105 @@
+"""Parity of the HIP path with the fp64 oracle, element by element (GPU).
+
+Small and ragged shapes compare every output element; the five named workloads
+at full size compare sampled rows (computed one by one by the oracle) and check
+properties of the whole output."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_attn_fwd_02_amd import workloads as W
+from gpu_helpers import TOL_LSE, TOL_O, check_full, compare, run_gpu, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+# (dtype, B, Hq, Hkv, Sq, Sk, D, causal)
+SHAPES = [
+    ("bf16", 1, 2, 2, 1, 1, 64, False),
+    ("bf16", 1, 2, 2, 1, 1, 128, True),
+    ("bf16", 1, 1, 1, 17, 17, 128, True),
+    ("bf16", 1, 2, 2, 127, 127, 64, False),
+    ("bf16", 2, 3, 3, 300, 300, 128, True),      # two query tiles, ragged tail
+    ("bf16", 1, 4, 1, 300, 513, 128, True),      # MQA, fewer queries than keys
+    ("bf16", 1, 4, 2, 513, 300, 64, True),       # more queries than keys: empty rows
+    ("bf16", 1, 8, 2, 1000, 1000, 128, True),    # GQA, several tiles
+    ("bf16", 2, 2, 2, 256, 64, 128, False),
+    ("bf16", 1, 2, 2, 64, 700, 64, False),
+    ("bf16", 1, 2, 2, 1, 700, 128, True),        # one query against many keys
+    ("bf16", 1, 2, 2, 700, 1, 128, True),        # many queries, one key
+    ("bf16", 1, 2, 2, 257, 257, 64, True),
+    ("fp16", 1, 2, 2, 300, 300, 128, True),
+    ("fp16", 1, 4, 2, 190, 260, 64, False),
+    ("fp16", 1, 8, 1, 513, 513, 128, True),
+    ("fp32", 1, 2, 2, 1, 1, 64, False),
+    ("fp32", 1, 2, 2, 300, 300, 128, True),
+    ("fp32", 1, 4, 2, 131, 77, 64, True),
+    ("fp32", 2, 4, 1, 70, 190, 128, False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=["%s_b%d_hq%d_hkv%d_sq%d_sk%d_d%d_%s" % (
+    s[0], *s[1:7], "causal" if s[7] else "full") for s in SHAPES])
+def test_shapes_full_output(shape):
+    dt, B, Hq, Hkv, Sq, Sk, D, causal = shape
+    w = W.custom(dt, B, Hq, Hkv, Sq, Sk, D, causal, seed=zlib.crc32(repr(shape).encode()) % 100000)
+    check_full(w)
+
+
+def test_small_fp32_workload():
+    check_full(W.WORKLOADS["mha_fp32_b1_h2_s128_d64"])
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5, 2.0])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_other_scales(scale, dt):
+    w = W.custom(dt, 1, 2, 1, 200, 333, 128, True, seed=77)
+    check_full(w, scale=scale)
+
+
+def test_no_lse_requested():
+    w = W.custom("bf16", 1, 2, 2, 300, 300, 64, True, seed=5)
+    check_full(w, want_lse=False)
+
+
+def test_peaky_small():
+    """Q, K with sigma 2 at D = 128: near one-hot rows (as the long-context workload)."""
+    w = W.custom("bf16", 1, 2, 2, 1024, 1024, 128, True, seed=1005,
+                 q_dist=("normal", 2.0), k_dist=("normal", 2.0))
+    check_full(w)
+
+
+def test_extreme_peaky_small():
+    """sigma 4: weights collapse onto one key; O must reproduce that V row."""
+    w = W.custom("bf16", 1, 2, 2, 512, 512, 128, False, seed=99,
+                 q_dist=("normal", 4.0), k_dist=("normal", 4.0))
+    check_full(w)
+
+
+FULL = [n for n in W.ORDER if n != "mha_fp32_b1_h2_s128_d64"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    """The named workloads at full size: sampled rows against the oracle, plus
+    whole-output properties (every value finite, every LSE finite since each
+    query sees at least one key)."""
+    w = W.WORKLOADS[name]
+    say("case", name, "(full size)")
+    q, k, v = W.make_inputs(w)
+    o, lse = run_gpu(q, k, v, w.causal, scale=w.scale)
+    assert torch.isfinite(o).all(), "non-finite O"
+    assert torch.isfinite(lse).all(), "non-finite LSE"
+    rows = sample_rows(w, 160, seed=w.seed)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, rows=rows)
+    og = o.reshape(-1, w.D)[torch.from_numpy(rows)]
+    lg = lse.reshape(-1)[torch.from_numpy(rows)]
+    e = compare(og, lg, o_ref, lse_ref, w.dtype, name)
+    say("  %d rows: max|dO| %.3g  max|dLSE| %.3g" % (len(rows), *e))
+    # whole-output property: rows of O lie inside the range of V (convex mixes)
+    vmin = v.to(torch.float32).amin().item()
+    vmax = v.to(torch.float32).amax().item()
+    of = o.to(torch.float32)
+    assert of.amin().item() >= vmin - TOL_O[w.dtype] and of.amax().item() <= vmax + TOL_O[w.dtype]
