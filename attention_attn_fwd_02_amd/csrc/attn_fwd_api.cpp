@@ -39,6 +39,11 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
     if (!product_fits(B, Hq, Sq, D) || !product_fits(B, Hkv, Sk, D)) return ATTN_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    // one (batch, head) slice of Q, K or V is addressed with 32-bit byte offsets
+    const int64_t esize = (dtype == ATTN_FP32) ? 4 : 2;
+    const int64_t slice_lim = (INT64_C(1) << 31) - (INT64_C(1) << 20);
+    if ((int64_t)Sq * D * esize > slice_lim || (int64_t)Sk * D * esize > slice_lim)
+        return ATTN_ERR_UNSUPPORTED;
 
     const KernelChoice kc = select_kernel(dtype, D, causal ? 1 : 0);
     if (!kc.fn) return ATTN_ERR_UNSUPPORTED;

@@ -11,22 +11,22 @@
 // follows the VDCores page ("VDCores: Resource Decoupled Programming and
 // Execution for Asynchronous GPUs", adaptive scheduling in its section 4.2).
 //
-// 16-bit path (bf16, fp16), per workgroup of 4 waves (one per SIMD):
-//   * the workgroup owns BM = 256 consecutive queries of one (batch, head); each
-//     wave owns 64 of them as two 32-query column blocks;
+// 16-bit path (bf16, fp16): workgroups of 4 waves, two workgroups per CU (two
+// waves per SIMD, so one wave's MFMAs overlap the other's softmax arithmetic):
+//   * the workgroup owns BM = 128 consecutive queries of one (batch, head); each
+//     wave owns 32 of them, one 32-query column block;
 //   * the wave computes S^T = K_tile . Q^T with v_mfma_f32_32x32x16_{bf16,f16}:
 //     K (keys x D) is the A operand read from LDS, Q^T the B operand held in
 //     VGPRs for the whole kernel.  In the 32x32 accumulator layout every lane
-//     holds one query column, so the row max and row sum of the online softmax
-//     are in-lane reductions plus one v_permlane32_swap between the two
-//     half-waves;
+//     holds one query column, so the row max and row sums of the online softmax
+//     are in-lane reductions plus one v_permlane32_swap between the half-waves;
 //   * the weights P^T are rounded to 16 bits in registers and feed the next MFMA
-//     directly as its B operand: O^T (D x queries) += V^T . P^T.  The key order
-//     inside each 16-key MFMA step is permuted so that P^T needs no data
-//     movement; V is stored transposed (and permuted to match) in LDS;
-//   * K and V tiles of 64 keys are double-buffered in LDS: the next tile's
-//     global loads are issued before the current tile's MFMAs and written to the
-//     other LDS buffer afterwards, one barrier per tile.
+//     directly as its B operand: O^T (D x queries) += V^T . P^T.  The A operand
+//     V^T comes from the row-major V tile through ds_read_b64_tr_b16 (the LDS
+//     transposing read), two reads per MFMA, in the key order P^T already has;
+//   * K and V tiles of 64 keys go from HBM to LDS by buffer_load ... lds (no
+//     VGPR staging; rows past Sk read as zero), XOR-swizzled per row against
+//     bank conflicts, double-buffered with one barrier per tile.
 // fp32 path: the same dataflow with v_mfma_f32_32x32x2_f32 (true fp32 products),
 // 32 queries per wave, 32-key tiles, single-buffered LDS.
 //
@@ -46,6 +46,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 
 #define NEG_INF (-__builtin_inff())
 
@@ -127,48 +129,48 @@ __device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
 // ---------------------------------------------------------------------------
 // 16-bit kernel
 // ---------------------------------------------------------------------------
-constexpr int NW = 4;            // waves per workgroup
-constexpr int QBLK = 2;          // 32-query column blocks per wave
-constexpr int BM16 = NW * QBLK * 32;
-constexpr int BN16 = 64;         // keys per tile
-
-template <int D> struct Lds16 {
-    static constexpr int KP = D + 8;         // K row pitch (elements): +16 B against bank conflicts
-    static constexpr int VP = BN16 + 8;      // V^T row pitch (elements)
-    static constexpr int K_ELEMS = BN16 * KP;
-    static constexpr int V_ELEMS = D * VP;
-    static constexpr int BUF = K_ELEMS + V_ELEMS;
-    static constexpr int BYTES = 2 * BUF * 2;  // two buffers of 16-bit elements
-};
-
-// Slot of key `kk` (0..63 within a tile) in a V^T row.  Inside every 16-key group
-// the 4-key chunks 1 and 2 trade places, so that lane half h of MFMA step t reads
-// its 8 keys {16t + 4h + 0..3, 16t + 8 + 4h + 0..3} as one contiguous 16-byte run,
-// matching the keys that P^T holds in accumulator registers 8(t%2) .. 8(t%2)+7.
-__device__ __forceinline__ int vt_slot(int kk) {
-    const int ch = (kk >> 2) & 3;
-    const int sw = (ch == 1) ? 2 : (ch == 2) ? 1 : ch;
-    return (kk & ~15) | (sw << 2) | (kk & 3);
-}
+constexpr int NW = 4;            // waves per workgroup (one per SIMD)
+constexpr int QPW = 32;          // queries per wave: one 32-column block of S^T / O^T
+constexpr int BM16 = NW * QPW;   // queries per workgroup
+constexpr int BN16 = 64;         // keys per tile (two 32-key blocks)
 
 // Weights are taken relative to a per-query reference m that is raised only when a
 // new score exceeds it by more than this many powers of two (then O and both sums
 // are rescaled exactly); in between, weights stay below 2^8, far from overflow.
 constexpr float RESCALE_LOG2 = 8.0f;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// LDS tiles are row-major [key][d] with 16-byte chunks XOR-swizzled inside each
+// row, so that both MFMA operand reads below are free of bank conflicts:
+//   K (ds_read_b128, 16 rows x one chunk per 16 lanes): chunk c of row r sits at c ^ kswz(r)
+//   V (ds_read_b64_tr_b16, 4 rows x 4 chunks per 32 lanes): chunk c of row r at c ^ vswz(r)
+template <int D> struct Tile16 {
+    static constexpr int ROW_BYTES = 2 * D;
+    static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BN16 * ROW_BYTES;   // one K or V tile
+    static constexpr int BUF_BYTES = 2 * TILE_BYTES;      // K then V
+    static __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    static __device__ __forceinline__ int vswz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // raw buffer: stride 0, num_records = bytes (loads past it return zero)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_16(AttnParams p) {
     typedef Elem16<DT> E;
     typedef typename E::vec8 vec8;
-    typedef Lds16<D> L;
+    typedef Tile16<D> T;
     constexpr int KSTEPS = D / 16;       // MFMA k-steps for S^T
     constexpr int DBLK = D / 32;         // 32-row blocks of O^T
-    constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
-    constexpr int K_ITERS = BN16 * CPR / 256;
-    constexpr int V_ITEMS = (BN16 / 4) * CPR;   // (4-key group, chunk) items
+    constexpr int DMA_PER_WAVE = T::TILE_BYTES / 1024 / NW;   // 1 KB per DMA instruction
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::BUF_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -180,229 +182,197 @@ void attn_fwd_16(AttnParams p) {
     const int kvh = tc.hq / (p.Hq / p.Hkv);
     const int off = p.Sk - p.Sq;
     const int qs = tc.qt * BM16;                 // first query of the workgroup
-    const int qw = qs + wave * (QBLK * 32);      // first query of this wave
+    const int qw = qs + wave * QPW;              // first query of this wave
 
-    const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + ((int64_t)(tc.b * p.Hq + tc.hq) * p.Sq) * D;
-    const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + ((int64_t)(tc.b * p.Hkv + kvh) * p.Sk) * D;
-    const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + ((int64_t)(tc.b * p.Hkv + kvh) * p.Sk) * D;
-    uint16_t* __restrict__ Og = (uint16_t*)p.o + ((int64_t)(tc.b * p.Hq + tc.hq) * p.Sq) * D;
+    const int64_t q_head = (int64_t)(tc.b * p.Hq + tc.hq) * p.Sq;
+    const int64_t kv_head = (int64_t)(tc.b * p.Hkv + kvh) * p.Sk;
+    const uint8_t* Qg = (const uint8_t*)p.q + q_head * (2 * D);
+    const uint8_t* Kg = (const uint8_t*)p.k + kv_head * (2 * D);
+    const uint8_t* Vg = (const uint8_t*)p.v + kv_head * (2 * D);
+    uint16_t* __restrict__ Og = (uint16_t*)p.o + q_head * D;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg, (uint32_t)p.Sq * (2 * D));
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg, (uint32_t)p.Sk * (2 * D));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg, (uint32_t)p.Sk * (2 * D));
 
-    // key range of the workgroup
+    // key range of the workgroup and of this wave
     const int last_q = min(qs + BM16, p.Sq) - 1;
     int kend = p.Sk;
     if (CAUSAL) kend = min(p.Sk, last_q + off + 1);
     const int ntiles = kend > 0 ? (kend + BN16 - 1) / BN16 : 0;
-    // key range of this wave
-    const int wlast_q = min(qw + QBLK * 32, p.Sq) - 1;
     int wkend = (qw < p.Sq) ? p.Sk : 0;
-    if (CAUSAL && qw < p.Sq) wkend = min(p.Sk, wlast_q + off + 1);
+    if (CAUSAL && qw < p.Sq) wkend = min(p.Sk, min(qw + QPW, p.Sq) - 1 + off + 1);
 
-    // ---- Q^T fragments (B operand), kept in registers for the whole kernel
-    vec8 qf[QBLK][KSTEPS];
+    // ---- Q^T fragments (B operand): lane (n, h) holds Q[qw + n][16s + 8h .. +7];
+    // rows past Sq read as zero
+    vec8 qf[KSTEPS];
     {
         const uint32_t qx = (p.q_mode == 1) ? 0x80008000u : 0u;
+        const uint32_t qz = (p.q_mode == 2) ? 0u : 0xffffffffu;
 #pragma unroll
-        for (int b = 0; b < QBLK; ++b) {
-            const int qrow = qw + 32 * b + n;
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                u32x4 raw = {0u, 0u, 0u, 0u};
-                if (qrow < p.Sq && p.q_mode != 2)
-                    raw = *(const u32x4*)(Qg + (int64_t)qrow * D + 16 * s + 8 * h);
-                raw ^= qx;
-                qf[b][s] = __builtin_bit_cast(vec8, raw);
-            }
+        for (int s = 0; s < KSTEPS; ++s) {
+            const uint32_t vo = (uint32_t)(qw + n) * (2 * D) + (16 * s + 8 * h) * 2;
+            u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, vo, 0, 0));
+            raw = (raw & qz) ^ qx;
+            qf[s] = __builtin_bit_cast(vec8, raw);
         }
     }
 
-    f32x16 oacc[DBLK][QBLK];
+    f32x16 oacc[DBLK];
 #pragma unroll
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-        for (int b = 0; b < QBLK; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[d][b][r] = 0.f;
+        for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
     // per query (this lane's column): reference m (log2 domain), and the partial
     // sums of this half-wave's weights in fp32 (le, for the LSE) and of the same
     // weights as rounded to 16 bits (lr, the normaliser of O, so that O is an
     // exactly normalised mix of V rows)
-    float m_run[QBLK], le_run[QBLK], lr_run[QBLK];
-#pragma unroll
-    for (int b = 0; b < QBLK; ++b) { m_run[b] = NEG_INF; le_run[b] = 0.f; lr_run[b] = 0.f; }
+    float m_run = NEG_INF, le_run = 0.f, lr_run = 0.f;
 
-    // ---- global -> register staging of one K/V tile
-    u32x4 kreg[K_ITERS];
-    u32x4 vreg[4];
-    const int kc = tid % CPR;            // K chunk handled by this thread
-    const int kr0 = tid / CPR;           // first K row handled by this thread
-    const bool v_item = tid < V_ITEMS;
-    const int vc = tid % CPR;            // V chunk
-    const int vg = tid / CPR;            // V 4-key group
-
-    auto load_tile = [&](int j) {
+    // ---- one K/V tile, global -> LDS directly (buffer_load ... lds), swizzled
+    auto dma_tile = [&](int j, uint8_t* __restrict__ dst) {
         const int k0 = j * BN16;
 #pragma unroll
-        for (int i = 0; i < K_ITERS; ++i) {
-            const int row = k0 + kr0 + i * (256 / CPR);
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (row < p.Sk) x = *(const u32x4*)(Kg + (int64_t)row * D + 8 * kc);
-            kreg[i] = x;
-        }
-        if (v_item) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = k0 + 4 * vg + i;
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (row < p.Sk) x = *(const u32x4*)(Vg + (int64_t)row * D + 8 * vc);
-                vreg[i] = x;
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint16_t* kb = smem + buf * L::BUF;
-        uint16_t* vb = kb + L::K_ELEMS;
-#pragma unroll
-        for (int i = 0; i < K_ITERS; ++i) {
-            const int row = kr0 + i * (256 / CPR);
-            *(u32x4*)(kb + row * L::KP + 8 * kc) = kreg[i];
-        }
-        if (v_item) {
-            const int slot = vt_slot(4 * vg);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // d = 8*vc + 2w (low halves) and 8*vc + 2w + 1 (high halves)
-                const uint32_t a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
-                u32x2 ev, od;
-                ev[0] = (a0 & 0xffffu) | (a1 << 16);
-                ev[1] = (a2 & 0xffffu) | (a3 << 16);
-                od[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                od[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-                *(u32x2*)(vb + (8 * vc + 2 * w) * L::VP + slot) = ev;
-                *(u32x2*)(vb + (8 * vc + 2 * w + 1) * L::VP + slot) = od;
-            }
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+            const int idx = (wave * DMA_PER_WAVE + i) * 64 + lane;   // 16-byte chunk in the tile
+            const int row = idx / T::CPR;
+            const int c = (idx % T::CPR);
+            const uint32_t lds_off = (uint32_t)(wave * DMA_PER_WAVE + i) * 1024;
+            const uint32_t kv = (uint32_t)(k0 + row) * (2 * D) + 16 * (c ^ T::kswz(row));
+            const uint32_t vv = (uint32_t)(k0 + row) * (2 * D) + 16 * (c ^ T::vswz(row));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + lds_off), 16, kv, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(dst + lds_off + T::TILE_BYTES), 16, vv, 0, 0, 0);
         }
     };
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
+    if (ntiles > 0) dma_tile(0, smem);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
 
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        const bool more = (j + 1) < ntiles;
-        if (more) load_tile(j + 1);
+    // One key tile: start the DMA of tile j+1 into `nxt`, then compute tile j from
+    // `cur`.  The two LDS buffers never overlap; saying so (__restrict__) lets the
+    // compiler read `cur` while the DMA into `nxt` is still in flight instead of
+    // waiting for it.  Tile j+1 is waited for (vmcnt) at the barrier after the step.
+    auto tile_step = [&](int j, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+        if (j + 1 < ntiles) dma_tile(j + 1, nxt);
 
-        const uint16_t* kb = smem + buf * L::BUF;
-        const uint16_t* vb = kb + L::K_ELEMS;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int ks0 = j * BN16 + 32 * sub;     // first key of this 32-key sub-tile
-            if (ks0 >= wkend) break;                 // above this wave's diagonal
+        const int k0 = j * BN16;
+        if (k0 < wkend) {
+            const uint8_t* kt = cur;
+            const uint8_t* vt = cur + T::TILE_BYTES;
 
-            // ---- S^T = K . Q^T for 32 keys x 64 queries
-            f32x16 sacc[QBLK];
+            // ---- S^T = K . Q^T  (two 32-key blocks)
+            f32x16 sacc[2];
 #pragma unroll
-            for (int b = 0; b < QBLK; ++b)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[b][r] = 0.f;
+                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s) {
-                const vec8 a = *(const vec8*)(kb + (32 * sub + n) * L::KP + 16 * s + 8 * h);
 #pragma unroll
-                for (int b = 0; b < QBLK; ++b) sacc[b] = E::mfma(a, qf[b][s], sacc[b]);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int row = 32 * kb + n;
+                    const vec8 a = *(const vec8*)(kt + row * T::ROW_BYTES + 16 * ((2 * s + h) ^ T::kswz(row)));
+                    sacc[kb] = E::mfma(a, qf[s], sacc[kb]);
+                }
             }
 
-            // ---- mask: causal diagonal sub-tiles and the ragged key tail
-            const bool need_mask = (ks0 + 32 > p.Sk) || (CAUSAL && (ks0 + 31 > qw + off));
+            // ---- mask: causal diagonal tiles and the ragged key tail
+            const bool need_mask = (k0 + BN16 > p.Sk) || (CAUSAL && (k0 + BN16 - 1 > qw + off));
             if (need_mask) {
+                const int qi = qw + n;
+                const int lim = CAUSAL ? min(p.Sk - 1, qi + off) : (p.Sk - 1);
 #pragma unroll
-                for (int b = 0; b < QBLK; ++b) {
-                    const int qi = qw + 32 * b + n;
-                    const int lim = CAUSAL ? min(p.Sk - 1, qi + off) : (p.Sk - 1);
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = ks0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key > lim) sacc[b][r] = NEG_INF;
+                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (key > lim) sacc[kb][r] = NEG_INF;
                     }
-                }
             }
 
             // ---- online softmax in the log2 domain: t = s * c, c = |scale| * log2(e)
-            float mx[QBLK];
-            bool raise = false;
+            float mx = NEG_INF;
 #pragma unroll
-            for (int b = 0; b < QBLK; ++b) {
-                float x = NEG_INF;
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[b][r]);
-                mx[b] = pair_max(x) * p.c;
-                raise |= mx[b] > m_run[b] + RESCALE_LOG2;
-            }
-            if (__any(raise)) {
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+            mx = pair_max(mx) * p.c;
+            if (__any(mx > m_run + RESCALE_LOG2)) {
                 // new reference = exact running max; rescale O and both sums
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+                m_run = m_new;
+                le_run *= alpha;
+                lr_run *= alpha;
 #pragma unroll
-                for (int b = 0; b < QBLK; ++b) {
-                    const float m_new = fmaxf(m_run[b], mx[b]);
-                    const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run[b] - m_new);
-                    m_run[b] = m_new;
-                    le_run[b] *= alpha;
-                    lr_run[b] *= alpha;
+                for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-                    for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[d][b][r] *= alpha;
-                }
+                    for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
             }
-            uint32_t pk[QBLK][8];
+            const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+            uint32_t pk[2][8];
+            float se = 0.f, sr = 0.f;
 #pragma unroll
-            for (int b = 0; b < QBLK; ++b) {
-                const float m_use = (m_run[b] == NEG_INF) ? 0.f : m_run[b];
-                float se = 0.f, sr = 0.f;
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
-                    const float p0 = fast_exp2(fmaf(sacc[b][r], p.c, -m_use));
-                    const float p1 = fast_exp2(fmaf(sacc[b][r + 1], p.c, -m_use));
+                    const float p0 = fast_exp2(fmaf(sacc[kb][r], p.c, -m_use));
+                    const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], p.c, -m_use));
                     se += p0;
                     se += p1;
                     const uint32_t w = E::pack(p0, p1);
-                    pk[b][r >> 1] = w;
+                    pk[kb][r >> 1] = w;
                     sr = E::dot2_ones(w, sr);
                 }
-                le_run[b] += se;
-                lr_run[b] += sr;
-            }
+            le_run += se;
+            lr_run += sr;
 
-            // ---- O^T += V^T . P^T  (two 16-key MFMA steps)
+            // ---- O^T += V^T . P^T  (four 16-key steps).  A operand from the row-major V
+            // tile by two transposing reads: lane l receives V[key0 + j][32db + (l % 32)],
+            // j = 0..3, with key0 = 16t + 8rr + 4h, which are exactly the keys that P^T
+            // holds in accumulator registers 8(t % 2) + 4rr + j.
+            const int tr_row = ((lane & 15) >> 2);
+            const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            const int tr_half = 8 * (lane & 1);
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int t = 2 * sub + hf;
-                vec8 bfr[QBLK];
-#pragma unroll
-                for (int b = 0; b < QBLK; ++b) {
-                    u32x4 w = {pk[b][4 * hf + 0], pk[b][4 * hf + 1], pk[b][4 * hf + 2], pk[b][4 * hf + 3]};
-                    bfr[b] = __builtin_bit_cast(vec8, w);
-                }
+            for (int t = 0; t < 4; ++t) {
+                const int kb = t >> 1, hf = t & 1;
+                u32x4 bw = {pk[kb][4 * hf + 0], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]};
+                const vec8 bfr = __builtin_bit_cast(vec8, bw);
 #pragma unroll
                 for (int d = 0; d < DBLK; ++d) {
-                    const vec8 a = *(const vec8*)(vb + (32 * d + n) * L::VP + 16 * t + 8 * h);
-#pragma unroll
-                    for (int b = 0; b < QBLK; ++b) oacc[d][b] = E::mfma(a, bfr[b], oacc[d][b]);
+                    short4_t lo, hi;
+                    {
+                        const int row = 16 * t + 4 * h + tr_row;
+                        const int c = 4 * d + tr_chunk;
+                        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_short4_t*)(vt + row * T::ROW_BYTES + 16 * (c ^ T::vswz(row)) + tr_half));
+                    }
+                    {
+                        const int row = 16 * t + 8 + 4 * h + tr_row;
+                        const int c = 4 * d + tr_chunk;
+                        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_short4_t*)(vt + row * T::ROW_BYTES + 16 * (c ^ T::vswz(row)) + tr_half));
+                    }
+                    short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    oacc[d] = E::mfma(__builtin_bit_cast(vec8, a8), bfr, oacc[d]);
                 }
             }
         }
 
-        if (more) store_tile(buf ^ 1);
+    };
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        tile_step(j, smem + buf * T::BUF_BYTES, smem + (buf ^ 1) * T::BUF_BYTES);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next tile's DMA has landed
         __syncthreads();
     }
 
     // ---- epilogue: O = O^T / lr, rounded once; LSE = ln2 * (m + log2 le)
-#pragma unroll
-    for (int b = 0; b < QBLK; ++b) {
-        const int qi = qw + 32 * b + n;
-        const float lr = pair_sum(lr_run[b]);
-        const float le = pair_sum(le_run[b]);
+    {
+        const int qi = qw + n;
+        const float lr = pair_sum(lr_run);
+        const float le = pair_sum(le_run);
         const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
         if (qi < p.Sq) {
             uint16_t* orow = Og + (int64_t)qi * D;
@@ -411,14 +381,13 @@ void attn_fwd_16(AttnParams p) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     u32x2 w;
-                    w[0] = E::pack(oacc[d][b][4 * g + 0] * inv, oacc[d][b][4 * g + 1] * inv);
-                    w[1] = E::pack(oacc[d][b][4 * g + 2] * inv, oacc[d][b][4 * g + 3] * inv);
+                    w[0] = E::pack(oacc[d][4 * g + 0] * inv, oacc[d][4 * g + 1] * inv);
+                    w[1] = E::pack(oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv);
                     *(u32x2*)(orow + 32 * d + 8 * g + 4 * h) = w;
                 }
             if (p.lse && h == 0) {
-                const float lse = (le > 0.f) ? (m_run[b] + __log2f(le)) * 0.69314718055994531f
-                                             : NEG_INF;
-                p.lse[(int64_t)(tc.b * p.Hq + tc.hq) * p.Sq + qi] = lse;
+                const float lse = (le > 0.f) ? (m_run + __log2f(le)) * 0.69314718055994531f : NEG_INF;
+                p.lse[q_head + qi] = lse;
             }
         }
     }

@@ -49,8 +49,9 @@ typedef enum {
     ATTN_ERR_INVALID_ARG = 1,   /* a null or misaligned pointer, a size < 1, Hq % Hkv != 0,
                                    a non-finite scale, an unknown dtype, or sizes whose
                                    element counts overflow 64-bit offsets */
-    ATTN_ERR_UNSUPPORTED = 2,   /* a head dimension D other than 64 or 128, or a grid too
-                                   large for one launch */
+    ATTN_ERR_UNSUPPORTED = 2,   /* a head dimension D other than 64 or 128, a grid too
+                                   large for one launch, or one (batch, head) slice of
+                                   q, k or v of 2 GiB - 1 MiB or more */
     ATTN_ERR_LAUNCH = 3         /* the HIP runtime refused the kernel launch */
 } attn_status_t;
 

@@ -102,6 +102,12 @@ def test_grid_too_large_is_unsupported(lib):
     assert _call(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Sq=1 << 20) == A.ATTN_ERR_UNSUPPORTED
 
 
+def test_huge_head_slice_is_unsupported(lib):
+    # one (batch, head) slice of K of 2^31 bytes: refused before any launch
+    assert _call(Sk=1 << 23, Sq=64) == A.ATTN_ERR_UNSUPPORTED
+    assert _call(Sq=1 << 23, Sk=64, causal=0) == A.ATTN_ERR_UNSUPPORTED
+
+
 def test_binding_refuses_host_tensors():
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
