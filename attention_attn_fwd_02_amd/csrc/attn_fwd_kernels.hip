@@ -25,8 +25,8 @@
 //     V^T comes from the row-major V tile through ds_read_b64_tr_b16 (the LDS
 //     transposing read), two reads per MFMA, in the key order P^T already has;
 //   * K and V tiles of 64 keys go from HBM to LDS by buffer_load ... lds (no
-//     VGPR staging; rows past Sk read as zero), XOR-swizzled per row against
-//     bank conflicts, double-buffered with one barrier per tile.
+//     VGPR staging; rows past Sk read as zero) into rows padded against bank
+//     conflicts, double-buffered with one barrier per tile.
 // fp32 path: the same dataflow with v_mfma_f32_32x32x2_f32 (true fp32 products),
 // 32 queries per wave, 32-key tiles, single-buffered LDS.
 //
@@ -142,23 +142,38 @@ constexpr float RESCALE_LOG2 = 8.0f;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-// LDS tiles are row-major [key][d] with 16-byte chunks XOR-swizzled inside each
-// row, so that both MFMA operand reads below are free of bank conflicts:
-//   K (ds_read_b128, 16 rows x one chunk per 16 lanes): chunk c of row r sits at c ^ kswz(r)
-//   V (ds_read_b64_tr_b16, 4 rows x 4 chunks per 32 lanes): chunk c of row r at c ^ vswz(r)
+// LDS tiles hold K and V row-major ([key][d]) with padded rows, chosen so that
+// both MFMA operand reads are free of bank conflicts (64 banks x 4 bytes):
+//   K, ds_read_b128: 16 lanes read one 16-byte slot of 16 consecutive rows; a
+//     pitch of 2D + 16 bytes puts those rows 16 bytes apart modulo 256;
+//   V, ds_read_b64_tr_b16: 32 lanes read 64 bytes of 4 consecutive rows; a pitch
+//     of 2D + 64 bytes puts those rows 64 bytes apart modulo 256.
+// Every operand read is then one lane base plus a compile-time offset.
 template <int D> struct Tile16 {
-    static constexpr int ROW_BYTES = 2 * D;
-    static constexpr int CPR = D / 8;                     // 16-byte chunks per row
-    static constexpr int TILE_BYTES = BN16 * ROW_BYTES;   // one K or V tile
-    static constexpr int BUF_BYTES = 2 * TILE_BYTES;      // K then V
-    static __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-    static __device__ __forceinline__ int vswz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+    static constexpr int ROW = 2 * D;                  // bytes of one K/V row in HBM
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int KPITCH = ROW + 16;
+    static constexpr int VPITCH = ROW + 64;
+    static constexpr int KSLOTS = KPITCH / 16;         // 16-byte LDS slots per K row
+    static constexpr int VSLOTS = VPITCH / 16;
+    static constexpr int KBYTES = BN16 * KPITCH;       // multiple of 1024
+    static constexpr int VBYTES = BN16 * VPITCH;
+    static constexpr int BUF = KBYTES + VBYTES;        // one K tile then one V tile
+    static constexpr int KDMA = KBYTES / 1024;         // 1 KB DMA instructions per K tile
+    static constexpr int VDMA = VBYTES / 1024;
+    static constexpr int KDMA_W = (KDMA + NW - 1) / NW;   // per wave (the last may be idle)
+    static constexpr int VDMA_W = (VDMA + NW - 1) / NW;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     // raw buffer: stride 0, num_records = bytes (loads past it return zero)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+// voffset that always lies past num_records (per-head slices are < 2^31 bytes and
+// the tile offset added through soffset is < 2^31): the DMA lane writes zeros
+// into a padding slot without touching memory.
+constexpr uint32_t OOB_VOFFSET = 0x7fff0000u;
 
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -168,13 +183,14 @@ void attn_fwd_16(AttnParams p) {
     typedef Tile16<D> T;
     constexpr int KSTEPS = D / 16;       // MFMA k-steps for S^T
     constexpr int DBLK = D / 32;         // 32-row blocks of O^T
-    constexpr int DMA_PER_WAVE = T::TILE_BYTES / 1024 / NW;   // 1 KB per DMA instruction
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::BUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wave index is uniform across the wave; readfirstlane tells the compiler,
+    // so every per-wave decision below is a scalar branch, not an exec mask
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31;     // query column (S^T, O^T) / key row (K) / d row (V^T)
     const int h = lane >> 5;     // half-wave
 
@@ -186,13 +202,13 @@ void attn_fwd_16(AttnParams p) {
 
     const int64_t q_head = (int64_t)(tc.b * p.Hq + tc.hq) * p.Sq;
     const int64_t kv_head = (int64_t)(tc.b * p.Hkv + kvh) * p.Sk;
-    const uint8_t* Qg = (const uint8_t*)p.q + q_head * (2 * D);
-    const uint8_t* Kg = (const uint8_t*)p.k + kv_head * (2 * D);
-    const uint8_t* Vg = (const uint8_t*)p.v + kv_head * (2 * D);
+    const uint8_t* Qg = (const uint8_t*)p.q + q_head * T::ROW;
+    const uint8_t* Kg = (const uint8_t*)p.k + kv_head * T::ROW;
+    const uint8_t* Vg = (const uint8_t*)p.v + kv_head * T::ROW;
     uint16_t* __restrict__ Og = (uint16_t*)p.o + q_head * D;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg, (uint32_t)p.Sq * (2 * D));
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg, (uint32_t)p.Sk * (2 * D));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg, (uint32_t)p.Sk * (2 * D));
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg, (uint32_t)p.Sq * T::ROW);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg, (uint32_t)p.Sk * T::ROW);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg, (uint32_t)p.Sk * T::ROW);
 
     // key range of the workgroup and of this wave
     const int last_q = min(qs + BM16, p.Sq) - 1;
@@ -210,7 +226,7 @@ void attn_fwd_16(AttnParams p) {
         const uint32_t qz = (p.q_mode == 2) ? 0u : 0xffffffffu;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const uint32_t vo = (uint32_t)(qw + n) * (2 * D) + (16 * s + 8 * h) * 2;
+            const uint32_t vo = (uint32_t)(qw + n) * T::ROW + (16 * s + 8 * h) * 2;
             u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, vo, 0, 0));
             raw = (raw & qz) ^ qx;
             qf[s] = __builtin_bit_cast(vec8, raw);
@@ -228,21 +244,40 @@ void attn_fwd_16(AttnParams p) {
     // exactly normalised mix of V rows)
     float m_run = NEG_INF, le_run = 0.f, lr_run = 0.f;
 
-    // ---- one K/V tile, global -> LDS directly (buffer_load ... lds), swizzled
-    auto dma_tile = [&](int j, uint8_t* __restrict__ dst) {
-        const int k0 = j * BN16;
+    // ---- DMA lane offsets (loop-invariant): DMA instruction i of this wave fills
+    // LDS slots 64*(wave + NW*i) + lane; a slot is (row, chunk) of the padded tile,
+    // and padding slots get an out-of-range offset
+    uint32_t kvo[T::KDMA_W], vvo[T::VDMA_W];
 #pragma unroll
-        for (int i = 0; i < DMA_PER_WAVE; ++i) {
-            const int idx = (wave * DMA_PER_WAVE + i) * 64 + lane;   // 16-byte chunk in the tile
-            const int row = idx / T::CPR;
-            const int c = (idx % T::CPR);
-            const uint32_t lds_off = (uint32_t)(wave * DMA_PER_WAVE + i) * 1024;
-            const uint32_t kv = (uint32_t)(k0 + row) * (2 * D) + 16 * (c ^ T::kswz(row));
-            const uint32_t vv = (uint32_t)(k0 + row) * (2 * D) + 16 * (c ^ T::vswz(row));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + lds_off), 16, kv, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(dst + lds_off + T::TILE_BYTES), 16, vv, 0, 0, 0);
-        }
+    for (int i = 0; i < T::KDMA_W; ++i) {
+        const int slot = 64 * (wave + NW * i) + lane;
+        const int row = slot / T::KSLOTS, c = slot % T::KSLOTS;
+        kvo[i] = (c < T::CPR) ? (uint32_t)(row * T::ROW + 16 * c) : OOB_VOFFSET;
+    }
+#pragma unroll
+    for (int i = 0; i < T::VDMA_W; ++i) {
+        const int slot = 64 * (wave + NW * i) + lane;
+        const int row = slot / T::VSLOTS, c = slot % T::VSLOTS;
+        vvo[i] = (c < T::CPR) ? (uint32_t)(row * T::ROW + 16 * c) : OOB_VOFFSET;
+    }
+    auto dma_tile = [&](int j, uint8_t* __restrict__ dst) {
+        const uint32_t so = (uint32_t)(j * BN16) * T::ROW;     // tile start, via soffset
+#pragma unroll
+        for (int i = 0; i < T::KDMA_W; ++i)
+            if (wave + NW * i < T::KDMA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + 1024 * (wave + NW * i)),
+                                                         16, kvo[i], so, 0, 0);
+#pragma unroll
+        for (int i = 0; i < T::VDMA_W; ++i)
+            if (wave + NW * i < T::VDMA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(dst + T::KBYTES + 1024 * (wave + NW * i)),
+                                                         16, vvo[i], so, 0, 0);
     };
+
+    // lane bases of the operand reads (bytes within one buffer)
+    const int k_lane = n * T::KPITCH + 16 * h;
+    const int tr_row = (lane & 15) >> 2;
+    const int v_lane = T::KBYTES + (4 * h + tr_row) * T::VPITCH + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
 
     if (ntiles > 0) dma_tile(0, smem);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
@@ -256,114 +291,101 @@ void attn_fwd_16(AttnParams p) {
         if (j + 1 < ntiles) dma_tile(j + 1, nxt);
 
         const int k0 = j * BN16;
-        if (k0 < wkend) {
-            const uint8_t* kt = cur;
-            const uint8_t* vt = cur + T::TILE_BYTES;
+        if (k0 >= wkend) return;             // tile wholly above this wave's diagonal
+        const uint8_t* kt = cur + k_lane;
+        const uint8_t* vt = cur + v_lane;
 
-            // ---- S^T = K . Q^T  (two 32-key blocks)
-            f32x16 sacc[2];
+        // ---- S^T = K . Q^T  (two 32-key blocks)
+        f32x16 sacc[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
+        for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int row = 32 * kb + n;
-                    const vec8 a = *(const vec8*)(kt + row * T::ROW_BYTES + 16 * ((2 * s + h) ^ T::kswz(row)));
-                    sacc[kb] = E::mfma(a, qf[s], sacc[kb]);
-                }
-            }
-
-            // ---- mask: causal diagonal tiles and the ragged key tail
-            const bool need_mask = (k0 + BN16 > p.Sk) || (CAUSAL && (k0 + BN16 - 1 > qw + off));
-            if (need_mask) {
-                const int qi = qw + n;
-                const int lim = CAUSAL ? min(p.Sk - 1, qi + off) : (p.Sk - 1);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key > lim) sacc[kb][r] = NEG_INF;
-                    }
-            }
-
-            // ---- online softmax in the log2 domain: t = s * c, c = |scale| * log2(e)
-            float mx = NEG_INF;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = pair_max(mx) * p.c;
-            if (__any(mx > m_run + RESCALE_LOG2)) {
-                // new reference = exact running max; rescale O and both sums
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
-                m_run = m_new;
-                le_run *= alpha;
-                lr_run *= alpha;
-#pragma unroll
-                for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-            }
-            const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
-            uint32_t pk[2][8];
-            float se = 0.f, sr = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = fast_exp2(fmaf(sacc[kb][r], p.c, -m_use));
-                    const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], p.c, -m_use));
-                    se += p0;
-                    se += p1;
-                    const uint32_t w = E::pack(p0, p1);
-                    pk[kb][r >> 1] = w;
-                    sr = E::dot2_ones(w, sr);
-                }
-            le_run += se;
-            lr_run += sr;
-
-            // ---- O^T += V^T . P^T  (four 16-key steps).  A operand from the row-major V
-            // tile by two transposing reads: lane l receives V[key0 + j][32db + (l % 32)],
-            // j = 0..3, with key0 = 16t + 8rr + 4h, which are exactly the keys that P^T
-            // holds in accumulator registers 8(t % 2) + 4rr + j.
-            const int tr_row = ((lane & 15) >> 2);
-            const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-            const int tr_half = 8 * (lane & 1);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int kb = t >> 1, hf = t & 1;
-                u32x4 bw = {pk[kb][4 * hf + 0], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]};
-                const vec8 bfr = __builtin_bit_cast(vec8, bw);
-#pragma unroll
-                for (int d = 0; d < DBLK; ++d) {
-                    short4_t lo, hi;
-                    {
-                        const int row = 16 * t + 4 * h + tr_row;
-                        const int c = 4 * d + tr_chunk;
-                        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_short4_t*)(vt + row * T::ROW_BYTES + 16 * (c ^ T::vswz(row)) + tr_half));
-                    }
-                    {
-                        const int row = 16 * t + 8 + 4 * h + tr_row;
-                        const int c = 4 * d + tr_chunk;
-                        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_short4_t*)(vt + row * T::ROW_BYTES + 16 * (c ^ T::vswz(row)) + tr_half));
-                    }
-                    short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    oacc[d] = E::mfma(__builtin_bit_cast(vec8, a8), bfr, oacc[d]);
-                }
+            for (int kb = 0; kb < 2; ++kb) {
+                const vec8 a = *(const vec8*)(kt + 32 * kb * T::KPITCH + 32 * s);
+                sacc[kb] = E::mfma(a, qf[s], sacc[kb]);
             }
         }
 
+        // ---- mask: causal diagonal tiles and the ragged key tail
+        const bool need_mask = (k0 + BN16 > p.Sk) || (CAUSAL && (k0 + BN16 - 1 > qw + off));
+        if (need_mask) {
+            const int qi = qw + n;
+            const int lim = (CAUSAL ? min(p.Sk - 1, qi + off) : (p.Sk - 1)) - (k0 + 4 * h);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * kb + 8 * (r >> 2) + (r & 3);    // relative to k0 + 4h
+                    if (key > lim) sacc[kb][r] = NEG_INF;
+                }
+        }
+
+        // ---- online softmax in the log2 domain: t = s * c, c = |scale| * log2(e)
+        float mp[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sacc[kb][r]);
+        float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+        mx = pair_max(mx) * p.c;
+        if (__any(mx > m_run + RESCALE_LOG2)) {
+            // new reference = exact running max; rescale O and both sums
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            le_run *= alpha;
+            lr_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+        }
+        const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+        uint32_t pk[2][8];
+        float se[4] = {0.f, 0.f, 0.f, 0.f}, sr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(sacc[kb][r], p.c, -m_use));
+                const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], p.c, -m_use));
+                se[r & 3] += p0;
+                se[(r & 3) + 1] += p1;
+                const uint32_t w = E::pack(p0, p1);
+                pk[kb][r >> 1] = w;
+                sr[(r >> 1) & 1] = E::dot2_ones(w, sr[(r >> 1) & 1]);
+            }
+        le_run += (se[0] + se[1]) + (se[2] + se[3]);
+        lr_run += sr[0] + sr[1];
+
+        // ---- O^T += V^T . P^T  (four 16-key steps).  A operand from the row-major V
+        // tile by two transposing reads: lane l receives V[key0 + j][32db + (l % 32)],
+        // j = 0..3, with key0 = 16t + 8rr + 4h, which are exactly the keys that P^T
+        // holds in accumulator registers 8(t % 2) + 4rr + j.
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int kb = t >> 1, hf = t & 1;
+            u32x4 bw = {pk[kb][4 * hf + 0], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]};
+            const vec8 bfr = __builtin_bit_cast(vec8, bw);
+#pragma unroll
+            for (int d = 0; d < DBLK; ++d) {
+                const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4_t*)(vt + (16 * t) * T::VPITCH + 64 * d));
+                const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4_t*)(vt + (16 * t + 8) * T::VPITCH + 64 * d));
+                const short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                oacc[d] = E::mfma(__builtin_bit_cast(vec8, a8), bfr, oacc[d]);
+            }
+        }
     };
+
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
-        tile_step(j, smem + buf * T::BUF_BYTES, smem + (buf ^ 1) * T::BUF_BYTES);
+        tile_step(j, smem + buf * T::BUF, smem + (buf ^ 1) * T::BUF);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next tile's DMA has landed
         __syncthreads();
     }
