@@ -27,8 +27,20 @@ def build(out: str = LIB, verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
+    _check_resolved(tmp)
     os.replace(tmp, out)
     return out
+
+
+def _check_resolved(lib: str) -> None:
+    """Every kernel launch stub must be defined in the library itself (a kernel
+    the host pass failed to emit shows up as an undefined attn_impl symbol)."""
+    res = subprocess.run(["nm", "-D", "--undefined-only", lib], check=True,
+                         capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in res.stdout.splitlines() if "attn_impl" in ln]
+    if missing:
+        os.remove(lib)
+        raise RuntimeError("kernel stubs missing from %s: %s" % (lib, ", ".join(missing)))
 
 
 def dump_asm(outdir: str) -> str:
