@@ -35,8 +35,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "attn_fwd_internal.h"
 
 namespace attn_impl {
@@ -131,8 +129,7 @@ __device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
 // ---------------------------------------------------------------------------
 // 16-bit kernel
 // ---------------------------------------------------------------------------
-constexpr int NW = 8;            // waves per workgroup (two per SIMD, in two groups)
-constexpr int NDMA = 4;          // waves that issue the tile loads (group 0)
+constexpr int NW = 4;            // waves per workgroup (one per SIMD)
 constexpr int QPW = 32;          // queries per wave: one 32-column block of S^T / O^T
 constexpr int BM16 = NW * QPW;   // queries per workgroup
 constexpr int BN16 = 64;         // keys per tile (two 32-key blocks)
@@ -161,10 +158,11 @@ template <int D> struct Tile16 {
     static constexpr int VSLOTS = VPITCH / 16;
     static constexpr int KBYTES = BN16 * KPITCH;       // multiple of 1024
     static constexpr int VBYTES = BN16 * VPITCH;
+    static constexpr int BUF = KBYTES + VBYTES;        // one K tile then one V tile
     static constexpr int KDMA = KBYTES / 1024;         // 1 KB DMA instructions per K tile
     static constexpr int VDMA = VBYTES / 1024;
-    static constexpr int KDMA_W = (KDMA + NDMA - 1) / NDMA;   // per loading wave
-    static constexpr int VDMA_W = (VDMA + NDMA - 1) / NDMA;
+    static constexpr int KDMA_W = (KDMA + NW - 1) / NW;   // per wave (the last may be idle)
+    static constexpr int VDMA_W = (VDMA + NW - 1) / NW;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -178,7 +176,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr uint32_t OOB_VOFFSET = 0x7fff0000u;
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_16(AttnParams p) {
     typedef Elem16<DT> E;
     typedef typename E::vec8 vec8;
@@ -186,7 +184,7 @@ void attn_fwd_16(AttnParams p) {
     constexpr int KSTEPS = D / 16;       // MFMA k-steps for S^T
     constexpr int DBLK = D / 32;         // 32-row blocks of O^T
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (T::KBYTES + T::VBYTES)];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::BUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -246,9 +244,9 @@ void attn_fwd_16(AttnParams p) {
     // exactly normalised mix of V rows)
     float m_run = NEG_INF, le_run = 0.f, lr_run = 0.f;
 
-    // ---- DMA lane offsets (loop-invariant): DMA instruction i of loading wave w
-    // (w < NDMA) fills LDS slots 64*(w + NDMA*i) + lane; a slot is (row, chunk) of
-    // the padded tile, and padding slots get an out-of-range offset
+    // ---- DMA lane offsets (loop-invariant): DMA instruction i of this wave fills
+    // LDS slots 64*(wave + NW*i) + lane; a slot is (row, chunk) of the padded tile,
+    // and padding slots get an out-of-range offset
     constexpr int KDMA_W = T::KDMA_W, VDMA_W = T::VDMA_W;
     // fixed bounds: an array sized by a template-dependent constant makes the host
     // compilation pass drop this kernel's launch stub
@@ -256,100 +254,94 @@ void attn_fwd_16(AttnParams p) {
     uint32_t kvo[8], vvo[8];
 #pragma unroll
     for (int i = 0; i < KDMA_W; ++i) {
-        const int slot = 64 * (wave + NDMA * i) + lane;
+        const int slot = 64 * (wave + NW * i) + lane;
         const int row = slot / T::KSLOTS, c = slot % T::KSLOTS;
         kvo[i] = (c < T::CPR) ? (uint32_t)(row * T::ROW + 16 * c) : OOB_VOFFSET;
     }
 #pragma unroll
     for (int i = 0; i < VDMA_W; ++i) {
-        const int slot = 64 * (wave + NDMA * i) + lane;
+        const int slot = 64 * (wave + NW * i) + lane;
         const int row = slot / T::VSLOTS, c = slot % T::VSLOTS;
         vvo[i] = (c < T::CPR) ? (uint32_t)(row * T::ROW + 16 * c) : OOB_VOFFSET;
     }
-    auto dma_k = [&](int j, uint8_t* __restrict__ dst) {
+    auto dma_tile = [&](int j, uint8_t* __restrict__ dst) {
         const uint32_t so = (uint32_t)(j * BN16) * T::ROW;     // tile start, via soffset
 #pragma unroll
         for (int i = 0; i < T::KDMA_W; ++i)
-            if (wave + NDMA * i < T::KDMA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + 1024 * (wave + NDMA * i)),
+            if (wave + NW * i < T::KDMA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + 1024 * (wave + NW * i)),
                                                          16, kvo[i], so, 0, 0);
-    };
-    auto dma_v = [&](int j, uint8_t* __restrict__ dst) {
-        const uint32_t so = (uint32_t)(j * BN16) * T::ROW;
 #pragma unroll
         for (int i = 0; i < T::VDMA_W; ++i)
-            if (wave + NDMA * i < T::VDMA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(dst + 1024 * (wave + NDMA * i)),
+            if (wave + NW * i < T::VDMA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(dst + T::KBYTES + 1024 * (wave + NW * i)),
                                                          16, vvo[i], so, 0, 0);
     };
 
-    // LDS: two K tiles, then two V tiles (K runs one tile ahead of V).
-    uint8_t* const kbuf0 = smem;
-    uint8_t* const kbuf1 = smem + T::KBYTES;
-    uint8_t* const vbuf0 = smem + 2 * T::KBYTES;
-    uint8_t* const vbuf1 = smem + 2 * T::KBYTES + T::VBYTES;
-
-    // lane bases of the operand reads (bytes within one K or V tile)
+    // lane bases of the operand reads (bytes within one buffer)
     const int k_lane = n * T::KPITCH + 16 * h;
     const int tr_row = (lane & 15) >> 2;
-    const int v_lane = (4 * h + tr_row) * T::VPITCH + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
+    const int v_lane = T::KBYTES + (4 * h + tr_row) * T::VPITCH + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
 
-    // tiles this wave takes part in (all waves take part in the loads)
-    const int wnt = wkend > 0 ? (wkend + BN16 - 1) / BN16 : 0;
+    if (ntiles > 0) dma_tile(0, smem);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
+    __syncthreads();
 
-    // ---- the pieces of one tile
-    // S^T = K . Q^T for the 64 keys of a tile (two 32-key blocks)
-    auto qk = [&](f32x16 (&s)[2], const uint8_t* kt) {
+    // One key tile: start the DMA of tile j+1 into `nxt`, then compute tile j from
+    // `cur`.  The two LDS buffers never overlap; saying so (__restrict__) lets the
+    // compiler read `cur` while the DMA into `nxt` is still in flight instead of
+    // waiting for it.  Tile j+1 is waited for (vmcnt) at the barrier after the step.
+    auto tile_step = [&](int j, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+        if (j + 1 < ntiles) dma_tile(j + 1, nxt);
+
+        const int k0 = j * BN16;
+        if (k0 >= wkend) return;             // tile wholly above this wave's diagonal
+        const uint8_t* kt = cur + k_lane;
+        const uint8_t* vt = cur + v_lane;
+
+        // ---- S^T = K . Q^T  (two 32-key blocks).  The MFMA bursts run at raised
+        // wave priority: when both waves of a SIMD have work, the one feeding the
+        // matrix cores issues first and the other fills the VALU meanwhile.
+        __builtin_amdgcn_s_setprio(2);
+        f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-        for (int st = 0; st < KSTEPS; ++st)
+        for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const vec8 a = *(const vec8*)(kt + k_lane + 32 * kb * T::KPITCH + 32 * st);
-                s[kb] = E::mfma(a, qf[st], s[kb]);
+                const vec8 a = *(const vec8*)(kt + 32 * kb * T::KPITCH + 32 * s);
+                sacc[kb] = E::mfma(a, qf[s], sacc[kb]);
             }
-        // keep only a few operand reads in flight ahead of the MFMAs (bounds VGPRs)
-        constexpr int NM = 2 * KSTEPS;
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-        for (int i = 0; i < NM - 3; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-    };
-    // does tile j reach past this wave's first query's diagonal, or past Sk?
-    auto needs_mask = [&](int j) {
-        const int k0 = j * BN16;
-        return (k0 + BN16 > p.Sk) || (CAUSAL && (k0 + BN16 - 1 > qw + off));
-    };
-    auto mask = [&](f32x16 (&s)[2], int j) {
-        const int qi = qw + n;
-        const int lim = (CAUSAL ? min(p.Sk - 1, qi + off) : (p.Sk - 1)) - (j * BN16 + 4 * h);
+
+        __builtin_amdgcn_s_setprio(0);
+        // ---- mask: causal diagonal tiles and the ragged key tail
+        const bool need_mask = (k0 + BN16 > p.Sk) || (CAUSAL && (k0 + BN16 - 1 > qw + off));
+        if (need_mask) {
+            const int qi = qw + n;
+            const int lim = (CAUSAL ? min(p.Sk - 1, qi + off) : (p.Sk - 1)) - (k0 + 4 * h);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * kb + 8 * (r >> 2) + (r & 3);    // relative to k0 + 4h
-                s[kb][r] = (key > lim) ? NEG_INF : s[kb][r];
-            }
-    };
-    // row max of a tile's scores, in the log2 domain (identical in both half-waves)
-    auto row_max = [&](f32x16 (&s)[2]) {
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * kb + 8 * (r >> 2) + (r & 3);    // relative to k0 + 4h
+                    if (key > lim) sacc[kb][r] = NEG_INF;
+                }
+        }
+
+        // ---- online softmax in the log2 domain: t = s * c, c = |scale| * log2(e)
         float mp[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kb][r]);
-        return pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * p.c;
-    };
-    // raise the reference m to the exact running max when a tile's max exceeds it by
-    // more than RESCALE_LOG2, rescaling O and both sums (wave-uniform, rare)
-    auto update_ref = [&](float mx) {
+            for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sacc[kb][r]);
+        float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+        mx = pair_max(mx) * p.c;
         if (__any(mx > m_run + RESCALE_LOG2)) {
+            // new reference = exact running max; rescale O and both sums
             const float m_new = fmaxf(m_run, mx);
             const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
             m_run = m_new;
@@ -360,17 +352,15 @@ void attn_fwd_16(AttnParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
         }
-    };
-    // weights P = 2^(t - m), their sums, and P packed to 16 bits (the B operand)
-    auto weights = [&](f32x16 (&s)[2], uint32_t (&pk)[2][8]) {
         const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+        uint32_t pk[2][8];
         float se[4] = {0.f, 0.f, 0.f, 0.f}, sr[2] = {0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(fmaf(s[kb][r], p.c, -m_use));
-                const float p1 = fast_exp2(fmaf(s[kb][r + 1], p.c, -m_use));
+                const float p0 = fast_exp2(fmaf(sacc[kb][r], p.c, -m_use));
+                const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], p.c, -m_use));
                 se[r & 3] += p0;
                 se[(r & 3) + 1] += p1;
                 const uint32_t w = E::pack(p0, p1);
@@ -379,12 +369,12 @@ void attn_fwd_16(AttnParams p) {
             }
         le_run += (se[0] + se[1]) + (se[2] + se[3]);
         lr_run += sr[0] + sr[1];
-    };
-    // O^T += V^T . P^T (four 16-key steps).  A operand from the row-major V tile by
-    // two transposing reads: lane l receives V[key0 + j][32db + (l % 32)], j = 0..3,
-    // key0 = 16t + 8rr + 4h, which are exactly the keys that P^T holds in
-    // accumulator registers 8(t % 2) + 4rr + j.
-    auto pv = [&](const uint8_t* vt, uint32_t (&pk)[2][8]) {
+
+        __builtin_amdgcn_s_setprio(2);
+        // ---- O^T += V^T . P^T  (four 16-key steps).  A operand from the row-major V
+        // tile by two transposing reads: lane l receives V[key0 + j][32db + (l % 32)],
+        // j = 0..3, with key0 = 16t + 8rr + 4h, which are exactly the keys that P^T
+        // holds in accumulator registers 8(t % 2) + 4rr + j.
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int kb = t >> 1, hf = t & 1;
@@ -393,76 +383,22 @@ void attn_fwd_16(AttnParams p) {
 #pragma unroll
             for (int d = 0; d < DBLK; ++d) {
                 const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4_t*)(vt + v_lane + (16 * t) * T::VPITCH + 64 * d));
+                    (lds_short4_t*)(vt + (16 * t) * T::VPITCH + 64 * d));
                 const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4_t*)(vt + v_lane + (16 * t + 8) * T::VPITCH + 64 * d));
+                    (lds_short4_t*)(vt + (16 * t + 8) * T::VPITCH + 64 * d));
                 const short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 oacc[d] = E::mfma(__builtin_bit_cast(vec8, a8), bfr, oacc[d]);
             }
         }
-        constexpr int NM = 4 * DBLK;
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int i = 0; i < NM - 3; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     };
 
-    // ---- ping-pong schedule.  The two waves that share a SIMD belong to the two
-    // groups (waves 0-3 and 4-7).  Every wave runs the same sequence of slots,
-    // separated by workgroup barriers: MFMA slot j [P.V of tile j-1, then S^T of tile
-    // j], VALU slot j [softmax of tile j].  Group 1 runs one slot behind group 0
-    // (one extra barrier at the start, group 0 one at the end), so while one wave of
-    // a SIMD feeds the matrix cores the other works on the vector ALU:
-    //   barrier interval 2j  : group 0 MFMA slot j     group 1 VALU slot j-1
-    //   barrier interval 2j+1: group 0 VALU slot j     group 1 MFMA slot j
-    // Both intervals read K(j) and V(j-1).  Group 0 loads K(j+1) and V(j) into the
-    // other two buffers during them and waits for its loads before the barrier that
-    // ends interval 2j+1.
-    const int group = wave >> 2;
-    // A barrier that only paces the slots: no data passes between waves across it,
-    // so no memory fence (which would also wait for this wave's DMA); nothing is
-    // scheduled across it.
-    auto slot_barrier = [] {
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    f32x16 sacc[2];
-    uint32_t pk[2][8];
-    // The LDS tiles are distinct (__restrict__): reads of K(j), V(j-1) need not
-    // wait for the DMA into the other two buffers.
-    auto step = [&](int j, const uint8_t* __restrict__ kread, const uint8_t* __restrict__ vread,
-                    uint8_t* __restrict__ kdma, uint8_t* __restrict__ vdma) {
-        if (group == 0) {
-            if (j + 1 < ntiles) dma_k(j + 1, kdma);
-            if (j < ntiles) dma_v(j, vdma);
-        }
-        // MFMA slot
-        if (j >= 1 && j - 1 < wnt) pv(vread, pk);
-        if (j < wnt) qk(sacc, kread);
-        slot_barrier();
-        // VALU slot: softmax of tile j
-        if (j < wnt) {
-            if (needs_mask(j)) mask(sacc, j);
-            update_ref(row_max(sacc));
-            weights(sacc, pk);
-        }
-        if (group == 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K(j+1), V(j) landed
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        tile_step(j, smem + buf * T::BUF, smem + (buf ^ 1) * T::BUF);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next tile's DMA has landed
         __syncthreads();
-    };
-
-    if (group == 0 && ntiles > 0) dma_k(0, kbuf0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
-    __syncthreads();
-    if (group == 1) slot_barrier();
-    for (int j = 0; j <= ntiles; ++j) {
-        const bool odd = j & 1;
-        step(j, odd ? kbuf1 : kbuf0, odd ? vbuf0 : vbuf1, odd ? kbuf0 : kbuf1, odd ? vbuf1 : vbuf0);
     }
-    if (group == 0) slot_barrier();
 
     // ---- epilogue: O = O^T / lr, rounded once; LSE = ln2 * (m + log2 le)
     {
@@ -649,7 +585,7 @@ KernelChoice select_kernel(int dtype, int D, int causal) {
         return kc;
     }
     kc.bm = BM16;
-    kc.threads = NW * 64;
+    kc.threads = 256;
     if (dtype == ATTN_IMPL_BF16)
         kc.fn = (D == 64) ? pick16<ATTN_IMPL_BF16, 64>(causal)
               : (D == 128) ? pick16<ATTN_IMPL_BF16, 128>(causal) : nullptr;

@@ -90,7 +90,10 @@ def cpu_baseline(w, q, k, v, target_s: float):
             return int(len(rows) * w.Sk)
         return int(np.clip(i + off + 1, 0, w.Sk).sum())
 
-    probe = rng.integers(0, total, size=16)
+    # calibrate on a warm oracle (the first call also loads the library and
+    # starts its threads), then size the timed sample for about target_s seconds
+    probe = rng.integers(0, total, size=256)
+    oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, rows=probe[:16])
     t0 = time.perf_counter()
     oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, rows=probe)
     t_probe = time.perf_counter() - t0
