@@ -25,7 +25,7 @@
  * Readings where the pages are silent (each one listed in the design notes):
  *   - layout: q, o are [B][Hq][Sq][D]; k, v are [B][Hkv][Sk][D]; lse is [B][Hq][Sq];
  *     all contiguous, D fastest.
- *   - grouped heads (the evaluation's GQA/MQA variants, "eight heads per group"):
+ *   - grouped heads (the evaluation's GQA/MQA variants, with groups of eight query heads):
  *     query head h reads key/value head h / (Hq / Hkv), i.e. consecutive groups.
  *   - causal mask with Sq != Sk: aligned bottom-right, key j is visible from query
  *     i iff j <= i + (Sk - Sq); a query with no visible key gets O = 0, LSE = -inf.
