@@ -299,10 +299,7 @@ void attn_fwd_16(AttnParams p) {
         const uint8_t* kt = cur + k_lane;
         const uint8_t* vt = cur + v_lane;
 
-        // ---- S^T = K . Q^T  (two 32-key blocks).  The MFMA bursts run at raised
-        // wave priority: when both waves of a SIMD have work, the one feeding the
-        // matrix cores issues first and the other fills the VALU meanwhile.
-        __builtin_amdgcn_s_setprio(2);
+        // ---- S^T = K . Q^T  (two 32-key blocks)
         f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -317,7 +314,6 @@ void attn_fwd_16(AttnParams p) {
             }
         }
 
-        __builtin_amdgcn_s_setprio(0);
         // ---- mask: causal diagonal tiles and the ragged key tail
         const bool need_mask = (k0 + BN16 > p.Sk) || (CAUSAL && (k0 + BN16 - 1 > qw + off));
         if (need_mask) {
@@ -370,7 +366,6 @@ void attn_fwd_16(AttnParams p) {
         le_run += (se[0] + se[1]) + (se[2] + se[3]);
         lr_run += sr[0] + sr[1];
 
-        __builtin_amdgcn_s_setprio(2);
         // ---- O^T += V^T . P^T  (four 16-key steps).  A operand from the row-major V
         // tile by two transposing reads: lane l receives V[key0 + j][32db + (l % 32)],
         // j = 0..3, with key0 = 16t + 8rr + 4h, which are exactly the keys that P^T
@@ -390,12 +385,25 @@ void attn_fwd_16(AttnParams p) {
                 oacc[d] = E::mfma(__builtin_bit_cast(vec8, a8), bfr, oacc[d]);
             }
         }
+        // interleave: weights of the first 32 keys, then P.V of those keys under the
+        // weights of the second 32, then the rest of P.V
+        __builtin_amdgcn_sched_group_barrier(0x002, 60, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * DBLK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * DBLK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
     };
 
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
         tile_step(j, smem + buf * T::BUF, smem + (buf ^ 1) * T::BUF);
-        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next tile's DMA has landed
         __syncthreads();
     }
