@@ -70,7 +70,13 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     const int64_t per_group = (int64_t)(Hq / Hkv) * p.nq;
     const int64_t nwg = groups * per_group;
     if (nwg > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
-    p.xcd_remap = (groups % 8 == 0) ? 1 : 0;
+    // Bundle enough key/value-head groups to fill the workgroup slots of one XCD
+    // (32 CUs x 2 workgroups), heaviest query tiles of the whole bundle first; the
+    // bundle count must divide the groups (and split over the 8 XCDs to remap).
+    int gb = 1;
+    while (gb * per_group < 64 && groups % (2 * gb) == 0) gb *= 2;
+    p.gbundle = gb;
+    p.xcd_remap = ((groups / gb) % 8 == 0) ? 1 : 0;
 
     void* args[] = {&p};
     const hipError_t err = hipLaunchKernel(kc.fn, dim3((unsigned)nwg), dim3(kc.threads), args, 0,

@@ -22,7 +22,8 @@ struct AttnParams {
     float c;          // |scale| * log2(e), strictly positive
     int q_mode;       // 0: use Q as is; 1: use -Q (negative scale); 2: use 0 (zero scale)
     int nq;           // query tiles per head
-    int xcd_remap;    // 1: give each XCD whole key/value-head groups
+    int xcd_remap;    // 1: give each XCD whole bundles of key/value-head groups
+    int gbundle;      // key/value-head groups per bundle (divides B * Hkv)
 };
 
 struct KernelChoice {

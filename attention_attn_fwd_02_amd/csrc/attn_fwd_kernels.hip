@@ -101,25 +101,32 @@ template <> struct Elem16<ATTN_IMPL_FP16> {
     }
 };
 
-// Workgroup -> (batch, query head, query tile).  Heavy causal tiles go first.
-// When the key/value-head groups split evenly over the 8 XCDs (workgroup w is
-// dispatched to XCD w % 8), every XCD gets whole groups, so all query heads and
-// query tiles that read one K/V head share that XCD's L2.
+// Workgroup -> (batch, query head, query tile).  Workgroups are taken in "bundles"
+// of p.gbundle consecutive key/value-head groups; inside a bundle the order is
+// query tile first (heaviest causal tiles of every head in the bundle before any
+// lighter one), then group, then query head.  A bundle is sized (on the host) to
+// fill the workgroup slots of an XCD, which keeps the causal tail balanced while
+// the K/V heads in flight stay few enough for one XCD's L2.  When the groups split
+// evenly over the 8 XCDs (workgroup w is dispatched to XCD w % 8), each XCD gets
+// whole bundles, so every query tile and query head that reads one K/V head runs
+// on the XCD that caches it.
 struct TileCoord { int b, hq, qt; };
 __device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
     const int R = p.Hq / p.Hkv;      // query heads per key/value head
-    const int U = R * p.nq;          // workgroups per key/value head
-    int g, u;
+    const int G = p.gbundle;         // key/value-head groups per bundle
+    const int BU = G * R * p.nq;     // workgroups per bundle
+    int bundle, u;
     if (p.xcd_remap) {
         const int xcd = w & 7, slot = w >> 3;
-        g = xcd + 8 * (slot / U);
-        u = slot % U;
+        bundle = xcd + 8 * (slot / BU);
+        u = slot % BU;
     } else {
-        g = w / U;
-        u = w % U;
+        bundle = w / BU;
+        u = w % BU;
     }
     TileCoord t;
-    t.qt = p.nq - 1 - u / R;
+    t.qt = p.nq - 1 - u / (G * R);
+    const int g = bundle * G + (u / R) % G;
     const int r = u % R;
     t.b = g / p.Hkv;
     t.hq = (g % p.Hkv) * R + r;
