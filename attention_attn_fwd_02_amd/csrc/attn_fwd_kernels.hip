@@ -26,7 +26,13 @@
 //     transposing read), two reads per MFMA, in the key order P^T already has;
 //   * K and V tiles of 64 keys go from HBM to LDS by buffer_load ... lds (no
 //     VGPR staging; rows past Sk read as zero) into rows padded against bank
-//     conflicts, double-buffered with one barrier per tile.
+//     conflicts, double-buffered with one barrier per tile, K one tile ahead of V;
+//   * each wave software-pipelines its tiles in two phases of 16 MFMAs: the
+//     scores of the next tile and P.V of the current one go to the matrix core
+//     while the VALU computes the weights of the other 32-key block, so the two
+//     units work on independent data;
+//   * the softmax reference m is raised only when needed (first visible keys, or
+//     a block whose weights sum past 2^8), so the common path has no max pass.
 // fp32 path: the same dataflow with v_mfma_f32_32x32x2_f32 (true fp32 products),
 // 32 queries per wave, 32-key tiles, single-buffered LDS.
 //
@@ -80,11 +86,6 @@ template <> struct Elem16<ATTN_IMPL_BF16> {
         bf16x2 v = {(__bf16)lo, (__bf16)hi};
         return __builtin_bit_cast(uint32_t, v);
     }
-    // acc + lo + hi of a packed pair, in fp32 (one v_dot2c with (1, 1))
-    static __device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-    }
 };
 template <> struct Elem16<ATTN_IMPL_FP16> {
     typedef f16x8 vec8;
@@ -94,10 +95,6 @@ template <> struct Elem16<ATTN_IMPL_FP16> {
     static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
         f16x2 v = {(_Float16)lo, (_Float16)hi};
         return __builtin_bit_cast(uint32_t, v);
-    }
-    static __device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
-        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
     }
 };
 
@@ -141,10 +138,11 @@ constexpr int QPW = 32;          // queries per wave: one 32-column block of S^T
 constexpr int BM16 = NW * QPW;   // queries per workgroup
 constexpr int BN16 = 64;         // keys per tile (two 32-key blocks)
 
-// Weights are taken relative to a per-query reference m that is raised only when a
-// new score exceeds it by more than this many powers of two (then O and both sums
-// are rescaled exactly); in between, weights stay below 2^8, far from overflow.
+// Weights are taken relative to a per-query reference m that is raised (and O and
+// the weight sum rescaled exactly) only when a 32-key block's weights sum past
+// 2^RESCALE_LOG2; every accepted weight is therefore below 2^8, far from overflow.
 constexpr float RESCALE_LOG2 = 8.0f;
+constexpr float RESCALE_SUM = 256.0f;      // 2^RESCALE_LOG2
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
@@ -191,7 +189,7 @@ void attn_fwd_16(AttnParams p) {
     constexpr int KSTEPS = D / 16;       // MFMA k-steps for S^T
     constexpr int DBLK = D / 32;         // 32-row blocks of O^T
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::BUF + 1024];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -245,11 +243,9 @@ void attn_fwd_16(AttnParams p) {
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
-    // per query (this lane's column): reference m (log2 domain), and the partial
-    // sums of this half-wave's weights in fp32 (le, for the LSE) and of the same
-    // weights as rounded to 16 bits (lr, the normaliser of O, so that O is an
-    // exactly normalised mix of V rows)
-    float m_run = NEG_INF, le_run = 0.f, lr_run = 0.f;
+    // per query (this lane's column): reference m (log2 domain) and the partial sum
+    // of this half-wave's weights, in fp32
+    float m_run = NEG_INF, le_run = 0.f;
 
     // ---- DMA lane offsets (loop-invariant): DMA instruction i of this wave fills
     // LDS slots 64*(wave + NW*i) + lane; a slot is (row, chunk) of the padded tile,
@@ -263,164 +259,228 @@ void attn_fwd_16(AttnParams p) {
     for (int i = 0; i < KDMA_W; ++i) {
         const int slot = 64 * (wave + NW * i) + lane;
         const int row = slot / T::KSLOTS, c = slot % T::KSLOTS;
-        kvo[i] = (c < T::CPR) ? (uint32_t)(row * T::ROW + 16 * c) : OOB_VOFFSET;
+        kvo[i] = (c < T::CPR && wave + NW * i < T::KDMA) ? (uint32_t)(row * T::ROW + 16 * c) : OOB_VOFFSET;
     }
 #pragma unroll
     for (int i = 0; i < VDMA_W; ++i) {
         const int slot = 64 * (wave + NW * i) + lane;
         const int row = slot / T::VSLOTS, c = slot % T::VSLOTS;
-        vvo[i] = (c < T::CPR) ? (uint32_t)(row * T::ROW + 16 * c) : OOB_VOFFSET;
+        vvo[i] = (c < T::CPR && wave + NW * i < T::VDMA) ? (uint32_t)(row * T::ROW + 16 * c) : OOB_VOFFSET;
     }
-    auto dma_tile = [&](int j, uint8_t* __restrict__ dst) {
-        const uint32_t so = (uint32_t)(j * BN16) * T::ROW;     // tile start, via soffset
+    // a tile past the workgroup's last one is "loaded" from an offset past
+    // num_records: the DMA then writes zeros and touches no memory, and the
+    // instruction needs no branch around it
+    auto tile_so = [&](int j) -> uint32_t {
+        return (j < ntiles) ? (uint32_t)(j * BN16) * T::ROW : OOB_VOFFSET;
+    };
+    auto dma_k = [&](int j, uint8_t* __restrict__ dst) {
+        const uint32_t so = tile_so(j);
 #pragma unroll
-        for (int i = 0; i < T::KDMA_W; ++i)
-            if (wave + NW * i < T::KDMA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + 1024 * (wave + NW * i)),
-                                                         16, kvo[i], so, 0, 0);
+        for (int i = 0; i < T::KDMA_W; ++i) {
+            // a wave's surplus instruction writes zeros into the spare slot past the buffers
+            uint8_t* d = (wave + NW * i < T::KDMA) ? dst + 1024 * (wave + NW * i) : smem + 2 * T::BUF;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)d, 16, kvo[i], so, 0, 0);
+        }
+    };
+    auto dma_v = [&](int j, uint8_t* __restrict__ dst) {
+        const uint32_t so = tile_so(j);
 #pragma unroll
-        for (int i = 0; i < T::VDMA_W; ++i)
-            if (wave + NW * i < T::VDMA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(dst + T::KBYTES + 1024 * (wave + NW * i)),
-                                                         16, vvo[i], so, 0, 0);
+        for (int i = 0; i < T::VDMA_W; ++i) {
+            uint8_t* d = (wave + NW * i < T::VDMA) ? dst + 1024 * (wave + NW * i) : smem + 2 * T::BUF;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)d, 16, vvo[i], so, 0, 0);
+        }
     };
 
-    // lane bases of the operand reads (bytes within one buffer)
+    // lane bases of the operand reads (bytes within one K or V tile)
     const int k_lane = n * T::KPITCH + 16 * h;
     const int tr_row = (lane & 15) >> 2;
-    const int v_lane = T::KBYTES + (4 * h + tr_row) * T::VPITCH + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
+    const int v_lane = (4 * h + tr_row) * T::VPITCH + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
 
-    if (ntiles > 0) dma_tile(0, smem);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
-    __syncthreads();
+    // K tiles live in kbuf(0/1), V tiles in vbuf(0/1); K runs one tile ahead of V
+    auto kbuf = [&](int i) -> uint8_t* { return smem + i * T::BUF; };
+    auto vbuf = [&](int i) -> uint8_t* { return smem + i * T::BUF + T::KBYTES; };
 
-    // One key tile: start the DMA of tile j+1 into `nxt`, then compute tile j from
-    // `cur`.  The two LDS buffers never overlap; saying so (__restrict__) lets the
-    // compiler read `cur` while the DMA into `nxt` is still in flight instead of
-    // waiting for it.  Tile j+1 is waited for (vmcnt) at the barrier after the step.
-    auto tile_step = [&](int j, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
-        if (j + 1 < ntiles) dma_tile(j + 1, nxt);
-
-        const int k0 = j * BN16;
-        if (k0 >= wkend) return;             // tile wholly above this wave's diagonal
-        const uint8_t* kt = cur + k_lane;
-        const uint8_t* vt = cur + v_lane;
-
-        // ---- S^T = K . Q^T  (two 32-key blocks)
-        f32x16 sacc[2];
+    // ---- S^T block kb (32 keys) of a tile: S^T = K . Q^T over the D/16 k-steps
+    auto qk_blk = [&](const uint8_t* __restrict__ kt, int kb, f32x16& sacc) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const vec8 a = *(const vec8*)(kt + 32 * kb * T::KPITCH + 32 * s);
-                sacc[kb] = E::mfma(a, qf[s], sacc[kb]);
-            }
+            const vec8 a = *(const vec8*)(kt + k_lane + 32 * kb * T::KPITCH + 32 * s);
+            sacc = E::mfma(a, qf[s], sacc);
         }
-
-        // ---- mask: causal diagonal tiles and the ragged key tail
-        const bool need_mask = (k0 + BN16 > p.Sk) || (CAUSAL && (k0 + BN16 - 1 > qw + off));
+    };
+    // ---- mask of block kb of tile j: causal diagonal and the ragged key tail
+    auto mask_blk = [&](int j, int kb, f32x16& sacc) {
+        const int k0 = j * BN16 + 32 * kb;
+        const bool need_mask = (k0 + 32 > p.Sk) || (CAUSAL && (k0 + 31 > qw + off));
         if (need_mask) {
             const int qi = qw + n;
             const int lim = (CAUSAL ? min(p.Sk - 1, qi + off) : (p.Sk - 1)) - (k0 + 4 * h);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * kb + 8 * (r >> 2) + (r & 3);    // relative to k0 + 4h
-                    if (key > lim) sacc[kb][r] = NEG_INF;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int key = 8 * (r >> 2) + (r & 3);    // relative to k0 + 4h
+                if (key > lim) sacc[r] = NEG_INF;
+            }
         }
-
-        // ---- online softmax in the log2 domain: t = s * c, c = |scale| * log2(e)
-        float mp[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    };
+    // ---- the reference m_run is raised to the max of a 32-key block (and of itself)
+    // only when needed: on a lane's first visible keys, and when the block's weights
+    // sum past 2^RESCALE_LOG2 (which every weight above that bound implies); O and
+    // the sum are rescaled with it.  Visible keys are a prefix of every row, so a
+    // block with none is followed by blocks with none.
+    auto raise_ref = [&](const f32x16& s) {
+        float mp[4] = {s[0], s[1], s[2], s[3]};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sacc[kb][r]);
+        for (int r = 4; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[r]);
         float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
         mx = pair_max(mx) * p.c;
-        if (__any(mx > m_run + RESCALE_LOG2)) {
-            // new reference = exact running max; rescale O and both sums
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
-            m_run = m_new;
-            le_run *= alpha;
-            lr_run *= alpha;
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        le_run *= alpha;
 #pragma unroll
-            for (int d = 0; d < DBLK; ++d)
+        for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-        }
+            for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+    };
+    // ---- weights of one 32-key block, packed to 16 bits; returns their fp32 sum
+    auto weights = [&](const f32x16& s, uint32_t (&pk)[8]) -> float {
         const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
-        uint32_t pk[2][8];
-        float se[4] = {0.f, 0.f, 0.f, 0.f}, sr[2] = {0.f, 0.f};
+        float se[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(fmaf(sacc[kb][r], p.c, -m_use));
-                const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], p.c, -m_use));
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(fmaf(s[r], p.c, -m_use));
+            const float p1 = fast_exp2(fmaf(s[r + 1], p.c, -m_use));
+            if (r < 4) {
+                se[r] = p0;
+                se[r + 1] = p1;
+            } else {
                 se[r & 3] += p0;
                 se[(r & 3) + 1] += p1;
-                const uint32_t w = E::pack(p0, p1);
-                pk[kb][r >> 1] = w;
-                sr[(r >> 1) & 1] = E::dot2_ones(w, sr[(r >> 1) & 1]);
             }
-        le_run += (se[0] + se[1]) + (se[2] + se[3]);
-        lr_run += sr[0] + sr[1];
-
-        // ---- O^T += V^T . P^T  (four 16-key steps).  A operand from the row-major V
-        // tile by two transposing reads: lane l receives V[key0 + j][32db + (l % 32)],
-        // j = 0..3, with key0 = 16t + 8rr + 4h, which are exactly the keys that P^T
-        // holds in accumulator registers 8(t % 2) + 4rr + j.
+            pk[r >> 1] = E::pack(p0, p1);
+        }
+        return (se[0] + se[1]) + (se[2] + se[3]);
+    };
+    // ---- O^T += V^T . P^T for one 32-key block (two 16-key steps).  A operand from
+    // the row-major V tile by two transposing reads: lane l receives
+    // V[key0 + j][32db + (l % 32)], j = 0..3, key0 = 16t + 8rr + 4h, exactly the keys
+    // that P^T holds in accumulator registers 8(t % 2) + 4rr + j.
+    auto pv_blk = [&](const uint8_t* __restrict__ vt, const uint32_t (&pk)[8], int kb) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int kb = t >> 1, hf = t & 1;
-            u32x4 bw = {pk[kb][4 * hf + 0], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]};
+        for (int hf = 0; hf < 2; ++hf) {
+            const int t = 2 * kb + hf;
+            u32x4 bw = {pk[4 * hf + 0], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
             const vec8 bfr = __builtin_bit_cast(vec8, bw);
 #pragma unroll
             for (int d = 0; d < DBLK; ++d) {
                 const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4_t*)(vt + (16 * t) * T::VPITCH + 64 * d));
+                    (lds_short4_t*)(vt + v_lane + (16 * t) * T::VPITCH + 64 * d));
                 const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4_t*)(vt + (16 * t + 8) * T::VPITCH + 64 * d));
+                    (lds_short4_t*)(vt + v_lane + (16 * t + 8) * T::VPITCH + 64 * d));
                 const short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 oacc[d] = E::mfma(__builtin_bit_cast(vec8, a8), bfr, oacc[d]);
             }
         }
-        // interleave: weights of the first 32 keys, then P.V of those keys under the
-        // weights of the second 32, then the rest of P.V
-        __builtin_amdgcn_sched_group_barrier(0x002, 60, 0);
+    };
+    // issue order inside a phase: KSTEPS score MFMAs (one K read each), then 2*DBLK
+    // P.V MFMAs (two V reads each), with the softmax VALU work of one block spread
+    // over all of them; LDS reads run three ahead of their MFMAs
+    auto phase_schedule = [&]() {
+        constexpr int NM = KSTEPS + 2 * DBLK;
+        constexpr int NR = KSTEPS + 4 * DBLK;
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * DBLK; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int i = 0; i < NM; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 2 * DBLK; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            // reads issued so far after this group: 3 + (K reads) + (V reads)
+            if (i < KSTEPS - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else if (3 + (KSTEPS - 3) + 2 * (i - (KSTEPS - 3)) + 2 <= NR) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            else if (3 + (KSTEPS - 3) + 2 * (i - (KSTEPS - 3)) + 1 <= NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     };
 
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        tile_step(j, smem + buf * T::BUF, smem + (buf ^ 1) * T::BUF);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next tile's DMA has landed
+    // ---- one software-pipelined step over key tile j.  On entry `s1` holds block 1
+    // of S(j) and `pk0` the weights of block 0 of tile j; on exit `n1` holds block 1
+    // of S(j+1) and `pk0` the weights of its block 0.
+    //   phase 1: S(j+1) block 0, O += P(j) block 0 . V, weights of S(j) block 1
+    //   phase 2: S(j+1) block 1, O += P(j) block 1 . V, weights of S(j+1) block 0
+    // The DMA of K(j+2) into `kd` and V(j+1) into `vd` runs meanwhile; `kr_` holds
+    // K(j+1) and `vr_` V(j).  The four buffers are distinct (__restrict__), so the
+    // compiler reads the two while the DMA into the other two is in flight.
+    auto step = [&](int j, f32x16& s1, uint32_t (&pk0)[8], f32x16& n0, f32x16& n1,
+                    uint8_t* __restrict__ kd, uint8_t* __restrict__ vd,
+                    const uint8_t* __restrict__ kr_, const uint8_t* __restrict__ vr_) {
+        if (j * BN16 >= wkend) {                        // tile wholly above this wave's diagonal
+            dma_k(j + 2, kd);
+            dma_v(j + 1, vd);
+            return;
+        }
+        const bool more = (j + 1) * BN16 < wkend;       // tile j+1 is visible to this wave
+        uint32_t pk1[8];
+        dma_k(j + 2, kd);
+        qk_blk(kr_, 0, n0);
+        pv_blk(vr_, pk0, 0);
+        float ts = weights(s1, pk1);
+        phase_schedule();
+        if (__any(ts > RESCALE_SUM)) {
+            raise_ref(s1);
+            ts = weights(s1, pk1);
+        }
+        le_run += ts;
+        if (more) {
+            mask_blk(j + 1, 0, n0);
+            if (__any(m_run == NEG_INF)) raise_ref(n0);
+        }
+        dma_v(j + 1, vd);
+        qk_blk(kr_, 1, n1);
+        pv_blk(vr_, pk1, 1);
+        float tn = weights(n0, pk0);
+        phase_schedule();
+        if (more && __any(tn > RESCALE_SUM)) {
+            raise_ref(n0);
+            tn = weights(n0, pk0);
+        }
+        le_run += more ? tn : 0.f;
+        if (more) mask_blk(j + 1, 1, n1);
+    };
+
+    f32x16 sa, sb, sn;
+    uint32_t pk0[8];
+    // prologue: K(0), V(0), K(1) in flight; scores of tile 0 and weights of its block 0
+    dma_k(0, kbuf(0));
+    dma_v(0, vbuf(0));
+    dma_k(1, kbuf(1));
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
+    __syncthreads();
+    if (0 < wkend && ntiles > 0) {
+        qk_blk(kbuf(0), 0, sn);
+        qk_blk(kbuf(0), 1, sa);
+        mask_blk(0, 0, sn);
+        mask_blk(0, 1, sa);
+        raise_ref(sn);
+        le_run += weights(sn, pk0);
+    }
+    __syncthreads();                      // K(0) is consumed before K(2) replaces it
+
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+        step(j, sa, pk0, sn, sb, kbuf(0), vbuf(1), kbuf(1), vbuf(0));
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        step(j + 1, sb, pk0, sn, sa, kbuf(1), vbuf(0), kbuf(0), vbuf(1));
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
+    if (j < ntiles) step(j, sa, pk0, sn, sb, kbuf(0), vbuf(1), kbuf(1), vbuf(0));
 
-    // ---- epilogue: O = O^T / lr, rounded once; LSE = ln2 * (m + log2 le)
+    // ---- epilogue: O = O^T / le, rounded once; LSE = ln2 * (m + log2 le)
     {
         const int qi = qw + n;
-        const float lr = pair_sum(lr_run);
         const float le = pair_sum(le_run);
-        const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
+        const float inv = (le > 0.f) ? 1.f / le : 0.f;
         if (qi < p.Sq) {
             uint16_t* orow = Og + (int64_t)qi * D;
 #pragma unroll
