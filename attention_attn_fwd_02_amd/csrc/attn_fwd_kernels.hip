@@ -11,9 +11,9 @@
 // follows the VDCores page ("VDCores: Resource Decoupled Programming and
 // Execution for Asynchronous GPUs", adaptive scheduling in its section 4.2).
 //
-// 16-bit path (bf16, fp16): workgroups of 4 waves, two workgroups per CU (two
+// 16-bit path (bf16, fp16): workgroups of 8 waves, one workgroup per CU (two
 // waves per SIMD, so one wave's MFMAs overlap the other's softmax arithmetic):
-//   * the workgroup owns BM = 128 consecutive queries of one (batch, head); each
+//   * the workgroup owns BM = 256 consecutive queries of one (batch, head); each
 //     wave owns 32 of them, one 32-query column block;
 //   * the wave computes S^T = K_tile . Q^T with v_mfma_f32_32x32x16_{bf16,f16}:
 //     K (keys x D) is the A operand read from LDS, Q^T the B operand held in
@@ -133,7 +133,7 @@ __device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
 // ---------------------------------------------------------------------------
 // 16-bit kernel
 // ---------------------------------------------------------------------------
-constexpr int NW = 4;            // waves per workgroup (one per SIMD)
+constexpr int NW = 8;            // waves per workgroup (two per SIMD, one workgroup per CU)
 constexpr int QPW = 32;          // queries per wave: one 32-column block of S^T / O^T
 constexpr int BM16 = NW * QPW;   // queries per workgroup
 constexpr int BN16 = 64;         // keys per tile (two 32-key blocks)
@@ -143,6 +143,32 @@ constexpr int BN16 = 64;         // keys per tile (two 32-key blocks)
 // 2^RESCALE_LOG2; every accepted weight is therefore below 2^8, far from overflow.
 constexpr float RESCALE_LOG2 = 8.0f;
 constexpr float RESCALE_SUM = 256.0f;      // 2^RESCALE_LOG2
+
+// Issue order inside one pipeline phase: KS score MFMAs (one K read each), then
+// 2*DB P.V MFMAs (two V reads each), with two VALU instructions of the softmax
+// after every MFMA (the rest of the softmax fills in behind them) and the LDS
+// reads kept PHASE_LOOKAHEAD MFMAs ahead of their use.
+constexpr int PHASE_VALU = 2;
+constexpr int PHASE_LOOKAHEAD = 2;
+// LDS reads that must have been issued before MFMA i of the phase
+template <int KS, int DB> constexpr int phase_reads(int i) {
+    return i >= KS + 2 * DB ? KS + 4 * DB : (i < KS ? i + 1 : KS + 2 * (i - KS + 1));
+}
+template <int KS, int DB, int I>
+__device__ __forceinline__ void phase_schedule_from() {
+    if constexpr (I < KS + 2 * DB) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, PHASE_VALU, 0);   // VALU
+        constexpr int more = phase_reads<KS, DB>(I + PHASE_LOOKAHEAD) - phase_reads<KS, DB>(I + PHASE_LOOKAHEAD - 1);
+        if constexpr (more > 0) __builtin_amdgcn_sched_group_barrier(0x100, more, 0);   // DS read
+        phase_schedule_from<KS, DB, I + 1>();
+    }
+}
+template <int KS, int DB>
+__device__ __forceinline__ void phase_schedule() {
+    __builtin_amdgcn_sched_group_barrier(0x100, phase_reads<KS, DB>(PHASE_LOOKAHEAD - 1), 0);
+    phase_schedule_from<KS, DB, 0>();
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
@@ -181,7 +207,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr uint32_t OOB_VOFFSET = 0x7fff0000u;
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_16(AttnParams p) {
     typedef Elem16<DT> E;
     typedef typename E::vec8 vec8;
@@ -384,24 +410,6 @@ void attn_fwd_16(AttnParams p) {
             }
         }
     };
-    // issue order inside a phase: KSTEPS score MFMAs (one K read each), then 2*DBLK
-    // P.V MFMAs (two V reads each), with the softmax VALU work of one block spread
-    // over all of them; LDS reads run three ahead of their MFMAs
-    auto phase_schedule = [&]() {
-        constexpr int NM = KSTEPS + 2 * DBLK;
-        constexpr int NR = KSTEPS + 4 * DBLK;
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            // reads issued so far after this group: 3 + (K reads) + (V reads)
-            if (i < KSTEPS - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            else if (3 + (KSTEPS - 3) + 2 * (i - (KSTEPS - 3)) + 2 <= NR) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            else if (3 + (KSTEPS - 3) + 2 * (i - (KSTEPS - 3)) + 1 <= NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-    };
-
     // ---- one software-pipelined step over key tile j.  On entry `s1` holds block 1
     // of S(j) and `pk0` the weights of block 0 of tile j; on exit `n1` holds block 1
     // of S(j+1) and `pk0` the weights of its block 0.
@@ -424,7 +432,7 @@ void attn_fwd_16(AttnParams p) {
         qk_blk(kr_, 0, n0);
         pv_blk(vr_, pk0, 0);
         float ts = weights(s1, pk1);
-        phase_schedule();
+        phase_schedule<KSTEPS, DBLK>();
         if (__any(ts > RESCALE_SUM)) {
             raise_ref(s1);
             ts = weights(s1, pk1);
@@ -438,7 +446,7 @@ void attn_fwd_16(AttnParams p) {
         qk_blk(kr_, 1, n1);
         pv_blk(vr_, pk1, 1);
         float tn = weights(n0, pk0);
-        phase_schedule();
+        phase_schedule<KSTEPS, DBLK>();
         if (more && __any(tn > RESCALE_SUM)) {
             raise_ref(n0);
             tn = weights(n0, pk0);
@@ -660,7 +668,7 @@ KernelChoice select_kernel(int dtype, int D, int causal) {
         return kc;
     }
     kc.bm = BM16;
-    kc.threads = 256;
+    kc.threads = 64 * NW;
     if (dtype == ATTN_IMPL_BF16)
         kc.fn = (D == 64) ? pick16<ATTN_IMPL_BF16, 64>(causal)
               : (D == 128) ? pick16<ATTN_IMPL_BF16, 128>(causal) : nullptr;
