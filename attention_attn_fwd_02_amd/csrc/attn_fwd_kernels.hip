@@ -215,7 +215,7 @@ void attn_fwd_16(AttnParams p) {
     constexpr int KSTEPS = D / 16;       // MFMA k-steps for S^T
     constexpr int DBLK = D / 32;         // 32-row blocks of O^T
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::BUF + 1024];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::BUF + 1024 + NW * QPW * (T::ROW + 16)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -484,26 +484,36 @@ void attn_fwd_16(AttnParams p) {
     }
     if (j < ntiles) step(j, sa, pk0, sn, sb, kbuf(0), vbuf(1), kbuf(1), vbuf(0));
 
-    // ---- epilogue: O = O^T / le, rounded once; LSE = ln2 * (m + log2 le)
+    // ---- epilogue: O = O^T / le, rounded once; LSE = ln2 * (m + log2 le).  The
+    // wave stages its 32 output rows in a private LDS tile (rows padded by 16 bytes)
+    // and stores them row-contiguously, 16 bytes per lane.
     {
         const int qi = qw + n;
         const float le = pair_sum(le_run);
         const float inv = (le > 0.f) ? 1.f / le : 0.f;
-        if (qi < p.Sq) {
-            uint16_t* orow = Og + (int64_t)qi * D;
+        constexpr int SPITCH = T::ROW + 16;
+        uint8_t* stg = smem + 2 * T::BUF + 1024 + wave * (QPW * SPITCH);
 #pragma unroll
-            for (int d = 0; d < DBLK; ++d)
+        for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2 w;
-                    w[0] = E::pack(oacc[d][4 * g + 0] * inv, oacc[d][4 * g + 1] * inv);
-                    w[1] = E::pack(oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv);
-                    *(u32x2*)(orow + 32 * d + 8 * g + 4 * h) = w;
-                }
-            if (p.lse && h == 0) {
-                const float lse = (le > 0.f) ? (m_run + __log2f(le)) * 0.69314718055994531f : NEG_INF;
-                p.lse[q_head + qi] = lse;
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = E::pack(oacc[d][4 * g + 0] * inv, oacc[d][4 * g + 1] * inv);
+                w[1] = E::pack(oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv);
+                *(u32x2*)(stg + n * SPITCH + 2 * (32 * d + 8 * g + 4 * h)) = w;
             }
+        constexpr int LPR = T::ROW / 16;          // lanes per row
+        constexpr int RPS = 64 / LPR;             // rows per store instruction
+#pragma unroll
+        for (int i = 0; i < QPW / RPS; ++i) {
+            const int row = RPS * i + lane / LPR;
+            const u32x4 v = *(const u32x4*)(stg + row * SPITCH + 16 * (lane % LPR));
+            if (qw + row < p.Sq)
+                *(u32x4*)((uint8_t*)Og + (int64_t)(qw + row) * T::ROW + 16 * (lane % LPR)) = v;
+        }
+        if (p.lse && h == 0 && qi < p.Sq) {
+            const float lse = (le > 0.f) ? (m_run + __log2f(le)) * 0.69314718055994531f : NEG_INF;
+            p.lse[q_head + qi] = lse;
         }
     }
 }
