@@ -104,6 +104,29 @@ HEADLINE = "mha_causal_bf16_b2_h32_s4096_d128"
 # The order the five workloads are listed in (smallest first).
 ORDER = list(WORKLOADS)
 
+# The rest of the pages' attention-variant set at their prefill shape (L_context 4096,
+# d_head 128; FIBER page, evaluation set-up): multi-query attention, grouped-query
+# attention with eight query heads per key/value head, and fp16 inputs.
+VARIANTS = {
+    w.name: w for w in [
+        Workload("mqa_causal_bf16_b2_hq32_hkv1_s4096_d128", "bf16", 2, 32, 1, 4096, 4096, 128,
+                 True, 1006, note="multi-query: all 32 query heads share one key/value head"),
+        Workload("gqa8_causal_bf16_b2_hq32_hkv4_s4096_d128", "bf16", 2, 32, 4, 4096, 4096, 128,
+                 True, 1007, note="grouped-query, 8 query heads per key/value head"),
+        Workload("mha_causal_fp16_b2_h32_s4096_d128", "fp16", 2, 32, 32, 4096, 4096, 128, True,
+                 1008, note="the headline shape with fp16 inputs"),
+    ]
+}
+
+
+def lookup(name: str) -> Workload:
+    """A named workload or attention variant."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in VARIANTS:
+        return VARIANTS[name]
+    raise KeyError("unknown workload %r (known: %s)" % (name, ", ".join(list(WORKLOADS) + list(VARIANTS))))
+
 
 def _draw(g, shape, dist):
     kind, p = dist

@@ -140,7 +140,7 @@ def main():
     from attention_attn_fwd_02_amd import workloads as W
     load_library()
     name = args.workload or W.HEADLINE
-    w = W.WORKLOADS[name]
+    w = W.lookup(name)
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     log("device: %s, %d CUs; workload %s" % (props.name, props.multi_processor_count, name))

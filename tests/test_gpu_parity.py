@@ -1,7 +1,7 @@
 """Parity of the HIP path with the fp64 oracle, element by element (GPU).
 
 Small and ragged shapes compare every output element; the five named workloads
-at full size compare sampled rows (computed one by one by the oracle) and check
+and the attention variants at full size compare sampled rows (computed one by one by the oracle) and check
 properties of the whole output."""
 import zlib
 
@@ -78,15 +78,15 @@ def test_extreme_peaky_small():
     check_full(w)
 
 
-FULL = [n for n in W.ORDER if n != "mha_fp32_b1_h2_s128_d64"]
+FULL = [n for n in W.ORDER if n != "mha_fp32_b1_h2_s128_d64"] + list(W.VARIANTS)
 
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
-    """The named workloads at full size: sampled rows against the oracle, plus
-    whole-output properties (every value finite, every LSE finite since each
-    query sees at least one key)."""
-    w = W.WORKLOADS[name]
+    """The named workloads and the attention variants (MQA, GQA-8, fp16) at full
+    size: sampled rows against the oracle, plus whole-output properties (every
+    value finite, every LSE finite since each query sees at least one key)."""
+    w = W.lookup(name)
     say("case", name, "(full size)")
     q, k, v = W.make_inputs(w)
     o, lse = run_gpu(q, k, v, w.causal, scale=w.scale)

@@ -1,4 +1,5 @@
 """The seeded input generator and the FLOP convention (CPU only)."""
+import pytest
 import torch
 
 from attention_attn_fwd_02_amd import workloads as W
@@ -46,3 +47,21 @@ def test_all_workloads_listed():
     assert W.WORKLOADS["mha_fp32_b1_h2_s128_d64"].dtype == "fp32"
     g = W.WORKLOADS["gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128"]
     assert g.Hq // g.Hkv == 4
+
+
+def test_attention_variants():
+    """MQA, GQA with eight query heads per K/V head, and fp16, all at L = 4096, d = 128."""
+    m = W.VARIANTS["mqa_causal_bf16_b2_hq32_hkv1_s4096_d128"]
+    g = W.VARIANTS["gqa8_causal_bf16_b2_hq32_hkv4_s4096_d128"]
+    f = W.VARIANTS["mha_causal_fp16_b2_h32_s4096_d128"]
+    assert m.Hkv == 1 and g.Hq // g.Hkv == 8 and f.dtype == "fp16"
+    for w in (m, g, f):
+        assert (w.Sq, w.Sk, w.D, w.causal) == (4096, 4096, 128, True)
+        # query-side work is the headline's: same FLOPs, fewer K/V bytes
+        assert w.flops() == W.WORKLOADS[W.HEADLINE].flops()
+        assert W.lookup(w.name) is w
+    assert m.min_hbm_bytes() < g.min_hbm_bytes() < f.min_hbm_bytes()
+    q, k, v = W.make_inputs(W.custom("fp16", 1, 2, 1, 8, 8, 64, True, seed=3))
+    assert q.dtype == torch.float16 and k.shape == (1, 1, 8, 64)
+    with pytest.raises(KeyError):
+        W.lookup("no_such_workload")
