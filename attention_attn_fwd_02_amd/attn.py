@@ -1,7 +1,7 @@
 """Thin Python binding of the C-ABI library `libattn_fwd.so` (include/attn_fwd.h).
 
 Argument marshalling only: every step of the attention forward runs in the HIP
-kernels behind `attn_fwd`.  PyTorch supplies device memory and the stream.  If
+kernels behind `attn_fwd` and `attn_fwd_decode`.  PyTorch supplies device memory and the stream.  If
 the library is missing this module raises; there is no fallback path.
 """
 import ctypes
@@ -39,6 +39,12 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd.restype = i32
     lib.attn_status_str.argtypes = [i32]
     lib.attn_status_str.restype = ctypes.c_char_p
+    sz = ctypes.c_size_t
+    lib.attn_fwd_decode_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.attn_fwd_decode_workspace.restype = i32
+    lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                    i32, vp, sz, vp]
+    lib.attn_fwd_decode.restype = i32
     _lib = lib
     return lib
 
@@ -47,6 +53,21 @@ def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, strea
     """The C entry point with raw integer pointers; returns the status code."""
     return load_library().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
                                    int(causal), int(dtype), stream)
+
+
+def attn_fwd_decode_workspace(B, Hq, Hkv, Sq, Sk, D, nsplit):
+    """(status, bytes) of the C workspace query."""
+    n = ctypes.c_size_t(0)
+    st = load_library().attn_fwd_decode_workspace(B, Hq, Hkv, Sq, Sk, D, int(nsplit), ctypes.byref(n))
+    return st, n.value
+
+
+def attn_fwd_decode(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, nsplit,
+                    workspace, workspace_bytes, stream) -> int:
+    """The C entry point with raw integer pointers; returns the status code."""
+    return load_library().attn_fwd_decode(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                          int(causal), int(dtype), int(nsplit), workspace,
+                                          int(workspace_bytes), stream)
 
 
 def attn_status_str(status: int) -> str:
@@ -67,17 +88,7 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True, st
     call is asynchronous on `stream` (default: torch's current stream).
     """
     import torch
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be device tensors")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k, v must share one dtype")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
-    B, Hq, Sq, D = q.shape
-    Bk, Hkv, Sk, Dk = k.shape
-    if v.shape != k.shape or Bk != B or Dk != D:
-        raise ValueError("shape mismatch: q%s k%s v%s" % (tuple(q.shape), tuple(k.shape),
-                                                          tuple(v.shape)))
+    B, Hq, Hkv, Sq, Sk, D = _check_inputs(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -90,6 +101,53 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True, st
                   lse.data_ptr() if want_lse else None,
                   B, Hq, Hkv, Sq, Sk, D, scale, causal, _dtype_code(q.dtype),
                   stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, (lse if want_lse else None)
+
+
+def _check_inputs(q, k, v):
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch: q%s k%s v%s" % (tuple(q.shape), tuple(k.shape),
+                                                          tuple(v.shape)))
+    return B, Hq, Hkv, Sq, Sk, D
+
+
+def fwd_decode(q, k, v, causal=False, scale=None, nsplit=0, out=None, lse=None, want_lse=True,
+               workspace=None, stream=None):
+    """Split-KV attention (few query rows per K/V head group) on torch device tensors.
+
+    Same tensors and result as `fwd` (bf16 or fp16 only; (Hq/Hkv)*Sq <= 32).  The
+    workspace (a uint8 device tensor) is allocated here when not given; reuse one
+    across calls on the same stream to avoid the allocation.
+    """
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _check_inputs(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st, need = attn_fwd_decode_workspace(B, Hq, Hkv, Sq, Sk, D, nsplit)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr() if want_lse else None, B, Hq, Hkv, Sq, Sk, D, scale,
+                         causal, _dtype_code(q.dtype), nsplit, workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return out, (lse if want_lse else None)

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_fwd.so")
-SOURCES = [os.path.join(CSRC, "attn_fwd_kernels.hip"), os.path.join(CSRC, "attn_fwd_api.cpp")]
+SOURCES = [os.path.join(CSRC, "attn_fwd_kernels.hip"), os.path.join(CSRC, "attn_decode_kernels.hip"),
+           os.path.join(CSRC, "attn_fwd_api.cpp")]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code (feature switched off).

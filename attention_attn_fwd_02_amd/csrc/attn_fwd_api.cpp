@@ -23,12 +23,9 @@ bool product_fits(int64_t a, int64_t b, int64_t c, int64_t d) {
     return true;
 }
 
-}  // namespace
-
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int Hq, int Hkv, int Sq, int Sk, int D,
-                        float scale, int causal, int dtype, hipStream_t stream) {
-    using namespace attn_impl;
+// Checks shared by both entry points (everything but the kernel choice).
+int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int dtype) {
     if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1) return ATTN_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
@@ -44,6 +41,51 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     const int64_t slice_lim = (INT64_C(1) << 31) - (INT64_C(1) << 20);
     if ((int64_t)Sq * D * esize > slice_lim || (int64_t)Sk * D * esize > slice_lim)
         return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+// log2(e) folded into the scale; its sign and a zero scale move onto Q
+void fold_scale(float scale, float* c, int* q_mode) {
+    const double cc = fabs((double)scale) * 1.4426950408889634;
+    *c = (scale == 0.0f) ? 1.0f : (float)cc;
+    *q_mode = (scale == 0.0f) ? 2 : (scale < 0.0f ? 1 : 0);
+}
+
+// Chunking of the keys for the split-KV pass.  nsplit_req <= 0 chooses: enough
+// chunks that about 1024 waves (four per CU) stream K/V at once, but no chunk
+// shorter than 256 keys.  Chunks are whole 32-key tiles; the count actually used
+// is ceil(Sk / chunk), which never exceeds the request.
+struct DecodePlan { int nsplit, chunk; };
+DecodePlan decode_plan(int B, int Hkv, int Sk, int nsplit_req) {
+    const int64_t groups = (int64_t)B * Hkv;
+    int64_t ns = nsplit_req;
+    if (ns <= 0) {
+        ns = (1024 + groups - 1) / groups;
+        const int64_t cap = (Sk + 255) / 256;
+        if (ns > cap) ns = cap;
+    }
+    if (ns < 1) ns = 1;
+    if (ns > Sk) ns = Sk;
+    int64_t chunk = (Sk + ns - 1) / ns;
+    chunk = (chunk + 31) / 32 * 32;
+    DecodePlan pl;
+    pl.chunk = (int)chunk;
+    pl.nsplit = (int)((Sk + chunk - 1) / chunk);
+    return pl;
+}
+
+size_t decode_workspace(int64_t rows, int D, int nsplit) {
+    return (size_t)nsplit * (size_t)rows * ((size_t)D + 1) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                        float scale, int causal, int dtype, hipStream_t stream) {
+    using namespace attn_impl;
+    const int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
+    if (st != ATTN_OK) return st;
 
     const KernelChoice kc = select_kernel(dtype, D, causal ? 1 : 0);
     if (!kc.fn) return ATTN_ERR_UNSUPPORTED;
@@ -59,10 +101,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.Hkv = Hkv;
     p.Sq = Sq;
     p.Sk = Sk;
-    // fold log2(e) into the scale; its sign and a zero scale are moved onto Q
-    const double c = fabs((double)scale) * 1.4426950408889634;
-    p.c = (scale == 0.0f) ? 1.0f : (float)c;
-    p.q_mode = (scale == 0.0f) ? 2 : (scale < 0.0f ? 1 : 0);
+    fold_scale(scale, &p.c, &p.q_mode);
     if (!(p.c > 0.0f) || !isfinite(p.c)) return ATTN_ERR_INVALID_ARG;
     p.nq = (Sq + kc.bm - 1) / kc.bm;
 
@@ -70,9 +109,9 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     const int64_t per_group = (int64_t)(Hq / Hkv) * p.nq;
     const int64_t nwg = groups * per_group;
     if (nwg > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
-    // Bundle enough key/value-head groups to fill the workgroup slots of one XCD
-    // (32 CUs x 2 workgroups), heaviest query tiles of the whole bundle first; the
-    // bundle count must divide the groups (and split over the 8 XCDs to remap).
+    // Bundle key/value-head groups until a bundle holds at least 64 workgroups (two
+    // rounds of an XCD's 32 CUs), heaviest query tiles of the whole bundle first;
+    // the bundle count must divide the groups (and split over the 8 XCDs to remap).
     int gb = 1;
     while (gb * per_group < 64 && groups % (2 * gb) == 0) gb *= 2;
     p.gbundle = gb;
@@ -82,6 +121,71 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     const hipError_t err = hipLaunchKernel(kc.fn, dim3((unsigned)nwg), dim3(kc.threads), args, 0,
                                            stream);
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" int attn_fwd_decode_workspace(int B, int Hq, int Hkv, int Sq, int Sk, int D, int nsplit,
+                                         size_t* bytes) {
+    using namespace attn_impl;
+    if (!bytes) return ATTN_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1 || Hq % Hkv != 0)
+        return ATTN_ERR_INVALID_ARG;
+    if (!product_fits(B, Hq, Sq, D) || !product_fits(B, Hkv, Sk, D)) return ATTN_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)(Hq / Hkv) * Sq > 32) return ATTN_ERR_UNSUPPORTED;
+    const DecodePlan pl = decode_plan(B, Hkv, Sk, nsplit);
+    *bytes = decode_workspace((int64_t)B * Hq * Sq, D, pl.nsplit);
+    return ATTN_OK;
+}
+
+extern "C" int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                               float scale, int causal, int dtype, int nsplit,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    using namespace attn_impl;
+    const int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    if (dtype == ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)(Hq / Hkv) * Sq > 32) return ATTN_ERR_UNSUPPORTED;
+    const DecodePlan pl = decode_plan(B, Hkv, Sk, nsplit);
+    const int64_t rows = (int64_t)B * Hq * Sq;
+    const size_t need = decode_workspace(rows, D, pl.nsplit);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
+    const int64_t nwg = (int64_t)B * Hkv * pl.nsplit;
+    if (nwg > INT32_MAX || rows > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    const void* fs = select_decode_split(dtype, D, causal ? 1 : 0);
+    const void* fm = select_decode_merge(dtype, D);
+    if (!fs || !fm) return ATTN_ERR_UNSUPPORTED;
+
+    DecodeParams dp;
+    dp.q = q;
+    dp.k = k;
+    dp.v = v;
+    dp.opart = (float*)workspace;
+    dp.lpart = dp.opart + (size_t)pl.nsplit * (size_t)rows * (size_t)D;
+    dp.B = B;
+    dp.Hq = Hq;
+    dp.Hkv = Hkv;
+    dp.Sq = Sq;
+    dp.Sk = Sk;
+    fold_scale(scale, &dp.c, &dp.q_mode);
+    if (!(dp.c > 0.0f) || !isfinite(dp.c)) return ATTN_ERR_INVALID_ARG;
+    dp.chunk = pl.chunk;
+    dp.nsplit = pl.nsplit;
+    void* a1[] = {&dp};
+    if (hipLaunchKernel(fs, dim3((unsigned)nwg), dim3(64), a1, 0, stream) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+
+    MergeParams mp;
+    mp.opart = dp.opart;
+    mp.lpart = dp.lpart;
+    mp.o = o;
+    mp.lse = lse;
+    mp.rows = rows;
+    mp.nsplit = pl.nsplit;
+    void* a2[] = {&mp};
+    if (hipLaunchKernel(fm, dim3((unsigned)rows), dim3(D), a2, 0, stream) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    return ATTN_OK;
 }
 
 extern "C" const char* attn_status_str(int status) {

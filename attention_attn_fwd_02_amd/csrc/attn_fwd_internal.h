@@ -34,6 +34,33 @@ struct KernelChoice {
 
 KernelChoice select_kernel(int dtype, int D, int causal);
 
+// Split-KV pass for few query rows: one wave per (batch, K/V head, chunk).
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    float* opart;     // [nsplit][B*Hq*Sq][D]: each chunk's O, normalised over the chunk
+    float* lpart;     // [nsplit][B*Hq*Sq]: each chunk's natural-log LSE (-inf: no visible key)
+    int B, Hq, Hkv, Sq, Sk;
+    float c;          // |scale| * log2(e), strictly positive
+    int q_mode;       // as in AttnParams
+    int chunk;        // keys per chunk, a multiple of 32
+    int nsplit;       // chunks per (batch, K/V head); workgroup w = (b*Hkv + g) * nsplit + chunk
+};
+
+// Merge of the chunks' partial results into O and LSE.
+struct MergeParams {
+    const float* opart;
+    const float* lpart;
+    void* o;          // [B*Hq*Sq][D], 16-bit element type
+    float* lse;       // may be null
+    int64_t rows;     // B*Hq*Sq
+    int nsplit;
+};
+
+const void* select_decode_split(int dtype, int D, int causal);   // null: unsupported
+const void* select_decode_merge(int dtype, int D);
+
 }  // namespace attn_impl
 
 #endif

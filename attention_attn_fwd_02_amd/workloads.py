@@ -119,13 +119,28 @@ VARIANTS = {
 }
 
 
+# Decoding (FIBER page, evaluation set-up: FlashDecoding with L_context = 4096 and
+# d_head = 128, several sequences with distinct KV caches): one new query row per
+# sequence and head against a 4096-key cache.  The batch sizes are a reading (the
+# page gives none), chosen so that each workload's K/V (1 GiB for MHA, 512 MiB for
+# GQA) exceeds the 256 MiB last-level cache and is measured against HBM.
+DECODE = {
+    w.name: w for w in [
+        Workload("decode_mha_bf16_b16_h32_sk4096_d128", "bf16", 16, 32, 32, 1, 4096, 128, True,
+                 1009, note="decode, multi-head: 16 sequences, 32 heads, 4096 cached keys"),
+        Workload("decode_gqa8_bf16_b64_hq32_hkv4_sk4096_d128", "bf16", 64, 32, 4, 1, 4096, 128,
+                 True, 1010, note="decode, grouped-query with 8 query heads per K/V head"),
+    ]
+}
+
+
 def lookup(name: str) -> Workload:
-    """A named workload or attention variant."""
-    if name in WORKLOADS:
-        return WORKLOADS[name]
-    if name in VARIANTS:
-        return VARIANTS[name]
-    raise KeyError("unknown workload %r (known: %s)" % (name, ", ".join(list(WORKLOADS) + list(VARIANTS))))
+    """A named workload, attention variant or decode workload."""
+    for table in (WORKLOADS, VARIANTS, DECODE):
+        if name in table:
+            return table[name]
+    raise KeyError("unknown workload %r (known: %s)" % (
+        name, ", ".join(list(WORKLOADS) + list(VARIANTS) + list(DECODE))))
 
 
 def _draw(g, shape, dist):

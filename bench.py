@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 KERNEL_SRC = os.path.join(ROOT, "attention_attn_fwd_02_amd", "csrc", "attn_fwd_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # dense MFMA peaks, MI355X
+HBM_PEAK_GBS = 8000.0                                             # HBM3E, MI355X
 
 
 def log(*a):
@@ -113,6 +114,36 @@ def cpu_baseline(w, q, k, v, target_s: float):
                       % (n, total, dt)}
 
 
+def decode_line(args, w, name, wall_ms, kern_ms):
+    """JSON line of a decode workload: bound by HBM bytes (K and V read once, Q read
+    and O, LSE written once), so the figure is GB/s against the 8 TB/s peak.  The
+    timed step is both kernels (split-KV pass and merge); the partial results they
+    exchange are not counted as algorithmic bytes."""
+    nbytes = w.min_hbm_bytes()
+    return {
+        "metric": "attention decode GB/s (split-KV, bf16, Sk=4096 D=128) + % of HBM peak",
+        "value": round(nbytes / (wall_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
+                   "Sk": w.Sk, "D": w.D, "causal": w.causal, "seed": w.seed,
+                   "bytes_per_step": nbytes, "flops_per_step": w.flops()},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (kern_ms * 1e-3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel_ms_per_launch": round(kern_ms, 5)},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,7 +167,7 @@ def main():
         copy_calibration(args.copy_mib, max(1, args.steps))
         return
 
-    from attention_attn_fwd_02_amd import fwd, load_library
+    from attention_attn_fwd_02_amd import fwd, fwd_decode, load_library
     from attention_attn_fwd_02_amd import workloads as W
     load_library()
     name = args.workload or W.HEADLINE
@@ -150,9 +181,22 @@ def main():
     o = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    decode = name in W.DECODE
+    if decode:
+        # split-KV pass + merge; the workspace is allocated once, outside the timing
+        from attention_attn_fwd_02_amd import attn_fwd_decode_workspace
+        st, nbytes = attn_fwd_decode_workspace(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, 0)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+        def step():
+            fwd_decode(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                       workspace=ws, stream=stream)
+    else:
+        def step():
+            fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
 
     for _ in range(args.warmup):
-        fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        step()
     torch.cuda.synchronize()
     log("warmup done (%d steps)" % args.warmup)
 
@@ -162,7 +206,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -174,6 +218,10 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     log("timed %d steps: %.3f ms/step wall, %.3f ms/launch (events), %.1f TFLOP/s"
         % (args.steps, wall_ms, kern_ms, achieved))
+
+    if decode:
+        print(json.dumps(decode_line(args, w, name, wall_ms, kern_ms)), flush=True)
+        return
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -29,6 +29,8 @@
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -85,6 +87,54 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int D,
              float scale, int causal, int dtype, hipStream_t stream);
+
+/*
+ * Split-KV attention for few query rows (decoding).
+ *
+ * The page "A Thread-Register Decoupled GPU Execution Model for Efficient Tensor
+ * Computation" evaluates decoding with FlashDecoding (evaluation set-up,
+ * "Workloads"; L_context = 4096, d_head = 128) and describes it in its results
+ * ("Decoding and Training Workloads Speedup") as matrix-vector work plus the
+ * softmax, bound by memory, with a distinct KV cache per sequence.  The result is
+ * the attention of attn_fwd above, computed in two passes: the keys of every
+ * (batch, K/V head) are cut into nsplit chunks streamed concurrently, each chunk
+ * giving an fp32 partial O normalised over its own keys and that chunk's
+ * log-sum-exp; a second kernel merges them exactly,
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * The query rows of one K/V head's group, (Hq / Hkv) * Sq of them, share every
+ * K/V byte read, so they must number at most 32.
+ *
+ * attn_fwd_decode_workspace -- bytes of device workspace attn_fwd_decode needs
+ * for these sizes and this nsplit; written to *bytes.  Returns ATTN_OK,
+ * ATTN_ERR_INVALID_ARG (a size < 1, Hq % Hkv != 0, null `bytes`, overflowing
+ * sizes) or ATTN_ERR_UNSUPPORTED (D not 64 or 128, (Hq / Hkv) * Sq > 32).
+ */
+int attn_fwd_decode_workspace(int B, int Hq, int Hkv, int Sq, int Sk, int D, int nsplit,
+                              size_t* bytes);
+
+/*
+ * attn_fwd_decode -- enqueue the two kernels on `stream`.
+ *
+ * q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal: exactly as for attn_fwd
+ * (same layouts, alignment, mask and empty-row convention), except that dtype
+ * must be ATTN_BF16 or ATTN_FP16 (ATTN_FP32 gives ATTN_ERR_UNSUPPORTED) and
+ * (Hq / Hkv) * Sq must be at most 32 (else ATTN_ERR_UNSUPPORTED).
+ *   nsplit           chunks per (batch, K/V head); <= 0 lets the library choose
+ *                    (about four waves per CU, chunks of at least 256 keys).
+ *                    Chunks are whole 32-key tiles, so the count used is
+ *                    ceil(Sk / chunk) and may be below the request.
+ *   workspace        device memory owned by the caller, 16-byte aligned, at least
+ *                    the size attn_fwd_decode_workspace reports for the same
+ *                    arguments (else ATTN_ERR_INVALID_ARG); overwritten, and in use
+ *                    until `stream` has run both kernels
+ *   workspace_bytes  its size
+ * The library allocates nothing.  Results are deterministic (fixed merge order);
+ * they differ from attn_fwd's by rounding only.
+ */
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                    float scale, int causal, int dtype, int nsplit,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a return code ("unknown status" otherwise). */
 const char* attn_status_str(int status);

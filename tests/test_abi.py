@@ -35,7 +35,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"attn_fwd", "attn_status_str"}, names
+    assert set(names) == {"attn_fwd", "attn_status_str", "attn_fwd_decode",
+                          "attn_fwd_decode_workspace"}, names
     raw = ctypes.CDLL(A.LIB_PATH)
     for nm in names:
         assert hasattr(raw, nm), nm
@@ -113,3 +114,78 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         A.fwd(q, q, q)
+
+
+
+# ---- split-KV decode entry points (every call below fails validation) ----
+W_ADDR = 0x60000
+DGOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=8, Hkv=2, Sq=1, Sk=4096, D=128, scale=0.125,
+             causal=1, dtype=A.ATTN_BF16, nsplit=0, ws=W_ADDR, ws_bytes=1 << 30, stream=None)
+
+
+def _dcall(**kw):
+    a = dict(DGOOD)
+    a.update(kw)
+    return A.attn_fwd_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                             a["Sq"], a["Sk"], a["D"], a["scale"], a["causal"], a["dtype"],
+                             a["nsplit"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _plan(B, Hkv, Sk, nsplit):
+    """The chunking the header documents, restated: about 1024 waves, chunks of at
+    least 256 keys, whole 32-key tiles; the count used is ceil(Sk / chunk)."""
+    if nsplit <= 0:
+        nsplit = min(-(-1024 // (B * Hkv)), -(-Sk // 256))
+    nsplit = max(1, min(nsplit, Sk))
+    chunk = -(-Sk // nsplit)
+    chunk = -(-chunk // 32) * 32
+    return -(-Sk // chunk), chunk
+
+
+@pytest.mark.parametrize("shape", [(16, 32, 32, 1, 4096, 128, 0), (2, 32, 4, 1, 4096, 128, 0),
+                                   (1, 32, 1, 1, 4096, 64, 0), (4, 8, 8, 4, 1000, 128, 7),
+                                   (1, 2, 2, 1, 17, 64, 0), (1, 1, 1, 1, 100000, 128, 1000)])
+def test_decode_workspace_size(lib, shape):
+    B, Hq, Hkv, Sq, Sk, D, ns = shape
+    st, nbytes = A.attn_fwd_decode_workspace(B, Hq, Hkv, Sq, Sk, D, ns)
+    assert st == A.ATTN_OK
+    used, chunk = _plan(B, Hkv, Sk, ns)
+    assert chunk % 32 == 0 and (used - 1) * chunk < Sk <= used * chunk
+    assert nbytes == used * B * Hq * Sq * (D + 1) * 4
+
+
+def test_decode_workspace_errors(lib):
+    assert A.attn_fwd_decode_workspace(0, 8, 2, 1, 64, 128, 0)[0] == A.ATTN_ERR_INVALID_ARG
+    assert A.attn_fwd_decode_workspace(1, 6, 4, 1, 64, 128, 0)[0] == A.ATTN_ERR_INVALID_ARG
+    assert A.attn_fwd_decode_workspace(1, 8, 2, 1, 64, 96, 0)[0] == A.ATTN_ERR_UNSUPPORTED
+    # 64 query heads on one K/V head are more rows than one MFMA block holds
+    assert A.attn_fwd_decode_workspace(1, 64, 1, 1, 64, 128, 0)[0] == A.ATTN_ERR_UNSUPPORTED
+    assert A.attn_fwd_decode_workspace(1, 8, 1, 5, 64, 128, 0)[0] == A.ATTN_ERR_UNSUPPORTED
+    assert A.load_library().attn_fwd_decode_workspace(1, 8, 2, 1, 64, 128, 0, None) == \
+        A.ATTN_ERR_INVALID_ARG
+
+
+DINVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(B=0), dict(Sk=0),
+    dict(Hq=6, Hkv=4), dict(scale=float("nan")), dict(dtype=7), dict(q=Q + 2), dict(lse=L + 1),
+    dict(ws=None), dict(ws=W_ADDR + 8), dict(ws_bytes=0), dict(ws_bytes=1000),
+]
+
+
+@pytest.mark.parametrize("bad", DINVALID, ids=[str(b) for b in DINVALID])
+def test_decode_invalid_arguments(lib, bad):
+    assert _dcall(**bad) == A.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(dtype=A.ATTN_FP32), dict(D=96), dict(Hq=64, Hkv=1),
+                                 dict(Sq=5, Hq=8, Hkv=1)],
+                         ids=["fp32", "d96", "mqa64", "rows40"])
+def test_decode_unsupported(lib, bad):
+    assert _dcall(**bad) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_decode_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.fwd_decode(q, q, q)
