@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the fused attention forward -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for the fused attention forward and its gradients -- TEST
+INFRASTRUCTURE ONLY.
 
 Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of
 `bench.py` may import this package.  The product path (the HIP library and its
@@ -66,6 +67,9 @@ class OracleLib:
         lib.oracle_attn_rows.restype = i32
         lib.oracle_widen.argtypes = [vp, i32, i64, vp]
         lib.oracle_widen.restype = i32
+        lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f64,
+                                        i32, vp, vp, vp, i32]
+        lib.oracle_attn_bwd.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         self.lib = lib
@@ -126,6 +130,33 @@ class OracleLib:
         return o, lse
 
 
+    def attn_bwd(self, q, k, v, do, causal=False, scale=None, nthreads=0):
+        """fp64 gradients (dq, dk, dv) of the attention forward for output
+        gradient `do` (same shape and storage dtype as q)."""
+        qr, qn = _as_raw(q)
+        kr, kn = _as_raw(k)
+        vr, vn = _as_raw(v)
+        gr, gn = _as_raw(do)
+        if not (qn == kn == vn == gn):
+            raise TypeError("oracle: q, k, v, do must share one dtype")
+        B, Hq, Sq, D = qr.shape
+        Bk, Hkv, Sk, Dk = kr.shape
+        if (Bk, Dk) != (B, D) or vr.shape != kr.shape or gr.shape != qr.shape:
+            raise ValueError("oracle: shape mismatch")
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        dq = np.empty(qr.shape, dtype=np.float64)
+        dk = np.empty(kr.shape, dtype=np.float64)
+        dv = np.empty(kr.shape, dtype=np.float64)
+        rc = self.lib.oracle_attn_bwd(qr.ctypes.data, kr.ctypes.data, vr.ctypes.data,
+                                      gr.ctypes.data, _DTYPE_CODE[qn], B, Hq, Hkv, Sq, Sk, D,
+                                      float(scale), int(bool(causal)), dq.ctypes.data,
+                                      dk.ctypes.data, dv.ctypes.data, int(nthreads))
+        if rc:
+            raise ValueError("oracle_attn_bwd failed (%d)" % rc)
+        return dq, dk, dv
+
+
 _default = None
 
 
@@ -143,6 +174,10 @@ def default() -> OracleLib:
 def attn_fwd(q, k, v, causal=False, scale=None, rows=None, nthreads=0):
     return default().attn_fwd(q, k, v, causal=causal, scale=scale, rows=rows,
                               nthreads=nthreads)
+
+
+def attn_bwd(q, k, v, do, causal=False, scale=None, nthreads=0):
+    return default().attn_bwd(q, k, v, do, causal=causal, scale=scale, nthreads=nthreads)
 
 
 def widen(x) -> np.ndarray:

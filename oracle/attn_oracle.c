@@ -35,7 +35,8 @@
  *
  * Parity status: every function here is pinned by the CPU tests (closed forms,
  * invariants, 50-digit brute force on tiny inputs, an independent library
- * routine); the pages print no attention values to pin against.
+ * routine; the gradients also by central differences of the forward); the pages
+ * print no attention values to pin against.
  */
 #include <math.h>
 #include <stddef.h>
@@ -187,6 +188,117 @@ int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype,
         }
         free(qrow);
         free(s);
+    }
+    return bad ? 2 : 0;
+}
+
+/*
+ * Gradients of the attention forward above (the FlashAttention backward the FIBER
+ * page evaluates as its training workload), written from the chain rule of
+ *     s_ij = scale q_i.k_j,  P_ij = exp(s_ij - LSE_i),  O_i = sum_j P_ij v_j
+ * for a loss whose gradient with respect to O is dO:
+ *     dv_j  = sum_i P_ij dO_i
+ *     dP_ij = dO_i . v_j
+ *     dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+ *     dq_i  = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i
+ * over visible pairs only; a key/value head's dk, dv sum over the query heads that
+ * read it.  P is recomputed in fp64 from the inputs (two-pass softmax per row).
+ *   q, dout : [B][Hq][Sq][D]   k, v : [B][Hkv][Sk][D]   (storage type `dtype`)
+ *   dq      : [B][Hq][Sq][D]   dk, dv : [B][Hkv][Sk][D]  (fp64, fully written)
+ * One thread per (batch, key/value head): no two threads touch the same output,
+ * and every sum runs in a fixed order.  Returns 0, 1 (invalid argument) or 2.
+ */
+int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                    int B, int Hq, int Hkv, int Sq, int Sk, int D, double scale, int causal,
+                    double* dq, double* dk, double* dv, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+    if (dtype < ORACLE_BF16 || dtype > ORACLE_FP64) return 1;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1) return 1;
+    if (Hq % Hkv != 0) return 1;
+    const int64_t groups = (int64_t)B * Hkv;
+    const int R = Hq / Hkv;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+        double* grow = (double*)malloc(sizeof(double) * (size_t)D);
+        double* p    = (double*)malloc(sizeof(double) * (size_t)Sk);
+        double* dp   = (double*)malloc(sizeof(double) * (size_t)Sk);
+        if (!qrow || !grow || !p || !dp) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t gi = 0; gi < groups; ++gi) {
+                const int64_t b = gi / Hkv, g = gi % Hkv;
+                const size_t kv_off = (size_t)gi * (size_t)Sk * (size_t)D;
+                for (size_t x = 0; x < (size_t)Sk * (size_t)D; ++x) {
+                    dk[kv_off + x] = 0.0;
+                    dv[kv_off + x] = 0.0;
+                }
+                for (int r = 0; r < R; ++r) {
+                    const int64_t h = g * R + r;
+                    for (int64_t i = 0; i < Sq; ++i) {
+                        const size_t row = (size_t)((b * Hq + h) * Sq + i);
+                        const size_t q_off = row * (size_t)D;
+                        double* dqi = dq + q_off;
+                        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+                        int64_t last = Sk - 1;
+                        if (causal) {
+                            const int64_t diag = i + ((int64_t)Sk - (int64_t)Sq);
+                            if (diag < last) last = diag;
+                        }
+                        if (last < 0) continue;                 /* no visible key: no gradient */
+                        for (int d = 0; d < D; ++d) {
+                            qrow[d] = load_elem(q, dtype, q_off + (size_t)d);
+                            grow[d] = load_elem(dout, dtype, q_off + (size_t)d);
+                        }
+                        /* scores, their max, and the normalised weights */
+                        double m = -INFINITY;
+                        for (int64_t j = 0; j <= last; ++j) {
+                            double dot = 0.0;
+                            const size_t koff = kv_off + (size_t)j * (size_t)D;
+                            for (int d = 0; d < D; ++d) dot += qrow[d] * load_elem(k, dtype, koff + (size_t)d);
+                            p[j] = scale * dot;
+                            if (p[j] > m) m = p[j];
+                        }
+                        double l = 0.0;
+                        for (int64_t j = 0; j <= last; ++j) {
+                            p[j] = exp(p[j] - m);
+                            l += p[j];
+                        }
+                        for (int64_t j = 0; j <= last; ++j) p[j] /= l;
+                        /* dP = dO . v and the row's sum of P dP */
+                        double pdp = 0.0;
+                        for (int64_t j = 0; j <= last; ++j) {
+                            double dot = 0.0;
+                            const size_t voff = kv_off + (size_t)j * (size_t)D;
+                            for (int d = 0; d < D; ++d) dot += grow[d] * load_elem(v, dtype, voff + (size_t)d);
+                            dp[j] = dot;
+                            pdp += p[j] * dot;
+                        }
+                        for (int64_t j = 0; j <= last; ++j) {
+                            const double ds = p[j] * (dp[j] - pdp);
+                            const size_t koff = kv_off + (size_t)j * (size_t)D;
+                            for (int d = 0; d < D; ++d) {
+                                dqi[d] += scale * ds * load_elem(k, dtype, koff + (size_t)d);
+                                dk[koff + (size_t)d] += scale * ds * qrow[d];
+                                dv[koff + (size_t)d] += p[j] * grow[d];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(qrow);
+        free(grow);
+        free(p);
+        free(dp);
     }
     return bad ? 2 : 0;
 }

@@ -371,6 +371,100 @@ def pin_row_subset(orc):
     assert np.array_equal(lse_r, lse.reshape(-1)[rows])
 
 
+# ----------------------------------------------------------------------------
+# 8. Gradients (the backward the FIBER page evaluates as its training workload).
+#    Central differences of the forward oracle -- itself pinned above -- fix every
+#    gradient on tiny fp64 inputs (causal and not, grouped heads, Sq != Sk with
+#    key-less rows, negative scales); a second library's automatic
+#    differentiation and three exact special cases pin them at larger shapes.
+# ----------------------------------------------------------------------------
+BWD_FD_SHAPES = [
+    (1, 1, 1, 4, 4, 3, False, 0.7),
+    (1, 2, 1, 5, 6, 4, True, 0.9),      # grouped heads, fewer queries than keys
+    (2, 2, 2, 6, 3, 2, True, -0.5),     # more queries than keys: rows without keys
+    (1, 4, 2, 3, 5, 3, False, 1.3),
+]
+
+
+def pin_bwd_finite_differences(orc):
+    rng = _rng(404)
+    h = 1e-6
+    for (B, Hq, Hkv, Sq, Sk, D, causal, scale) in BWD_FD_SHAPES:
+        q = _rand(rng, (B, Hq, Sq, D))
+        k = _rand(rng, (B, Hkv, Sk, D))
+        v = _rand(rng, (B, Hkv, Sk, D))
+        g = _rand(rng, (B, Hq, Sq, D))
+        dq, dk, dv = orc.attn_bwd(q, k, v, g, causal=causal, scale=scale)
+
+        def loss(qq, kk, vv):
+            o, _ = orc.attn_fwd(qq, kk, vv, causal=causal, scale=scale)
+            return float((o * g).sum())
+
+        for which, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[which]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[which]
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            err = np.abs(num - grad).max()
+            assert err < 1e-6 * max(1.0, np.abs(num).max()), (which, B, Hq, Hkv, Sq, Sk, err)
+
+
+def pin_bwd_special_cases(orc):
+    """Exact facts: (a) Q = 0 gives uniform weights, so dk = 0 and dv_j is the sum of
+    dO_i / |J_i| over the queries that see key j; (b) identical V rows make every
+    dP_ij of a row equal, so dS = 0 and dq = dk = 0; (c) the weights of a row sum
+    to one, so sum_j dv_j = sum of dO over rows that see any key."""
+    rng = _rng(405)
+    B, Hq, Hkv, Sq, Sk, D = 1, 2, 1, 5, 7, 3
+    k = _rand(rng, (B, Hkv, Sk, D))
+    v = _rand(rng, (B, Hkv, Sk, D))
+    g = _rand(rng, (B, Hq, Sq, D))
+    q0 = np.zeros((B, Hq, Sq, D))
+    for causal in (False, True):
+        dq, dk, dv = orc.attn_bwd(q0, k, v, g, causal=causal, scale=0.8)
+        assert np.all(dk == 0.0)
+        want = np.zeros((B, Hkv, Sk, D))
+        for h in range(Hq):
+            for i in range(Sq):
+                last = min(Sk - 1, i + Sk - Sq) if causal else Sk - 1
+                for j in range(last + 1):
+                    want[0, 0, j] += g[0, h, i] / (last + 1)
+        assert np.allclose(dv, want, rtol=0, atol=1e-13)
+        q = _rand(rng, (B, Hq, Sq, D))
+        vc = np.broadcast_to(_rand(rng, (1, 1, 1, D)), v.shape).copy()
+        dq, dk, dv = orc.attn_bwd(q, k, vc, g, causal=causal, scale=0.8)
+        assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13
+        dq, dk, dv = orc.attn_bwd(q, k, v, g, causal=causal, scale=0.8)
+        assert np.allclose(dv.sum(axis=2)[0, 0], g[0].sum(axis=(0, 1)), rtol=0, atol=1e-12)
+
+
+def pin_bwd_torch_autograd(orc):
+    """fp64 automatic differentiation of an explicit softmax attention in torch."""
+    g0 = torch.Generator().manual_seed(406)
+    for (B, Hq, Hkv, Sq, Sk, D, causal) in [(1, 2, 2, 40, 40, 16, True), (2, 4, 1, 24, 50, 8, True),
+                                           (1, 3, 3, 30, 20, 16, False)]:
+        q = (torch.randn(B, Hq, Sq, D, generator=g0, dtype=torch.float64) * 1.5).requires_grad_()
+        k = (torch.randn(B, Hkv, Sk, D, generator=g0, dtype=torch.float64) * 1.5).requires_grad_()
+        v = torch.randn(B, Hkv, Sk, D, generator=g0, dtype=torch.float64).requires_grad_()
+        go = torch.randn(B, Hq, Sq, D, generator=g0, dtype=torch.float64)
+        scale = 1.0 / math.sqrt(D)
+        kk = torch.repeat_interleave(k, Hq // Hkv, dim=1)
+        vv = torch.repeat_interleave(v, Hq // Hkv, dim=1)
+        scores = (q @ kk.transpose(-1, -2)) * scale
+        if causal:
+            mask = torch.ones(Sq, Sk, dtype=torch.bool).tril(diagonal=Sk - Sq)
+            scores = scores.masked_fill(~mask, -math.inf)
+        w = torch.softmax(scores, dim=-1).nan_to_num(0.0)
+        (w @ vv).backward(go)
+        dq, dk, dv = orc.attn_bwd(q.detach(), k.detach(), v.detach(), go, causal=causal, scale=scale)
+        for mine, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
+            assert np.allclose(mine, ref.numpy(), rtol=0, atol=1e-11), (B, Hq, Hkv, Sq, Sk)
+
+
 ALL_PINS = [
     pin_bruteforce_decimal,
     pin_hand_examples,
@@ -386,4 +480,7 @@ ALL_PINS = [
     pin_storage_widening,
     pin_torch_sdpa,
     pin_row_subset,
+    pin_bwd_finite_differences,
+    pin_bwd_special_cases,
+    pin_bwd_torch_autograd,
 ]

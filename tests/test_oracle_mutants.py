@@ -36,6 +36,14 @@ MUTANTS = [
     ("last_key_dropped", "for (int64_t j = 0; j <= last; ++j) {\n        const double w",
      "for (int64_t j = 0; j < last; ++j) {\n        const double w"),
     ("exp_weight_unused_in_sum", "l += w;", "l += 1.0;"),
+    ("bwd_drop_row_term", "const double ds = p[j] * (dp[j] - pdp);", "const double ds = p[j] * dp[j];"),
+    ("bwd_dk_unscaled", "dk[koff + (size_t)d] += scale * ds * qrow[d];",
+     "dk[koff + (size_t)d] += ds * qrow[d];"),
+    ("bwd_dv_from_ds", "dv[koff + (size_t)d] += p[j] * grow[d];", "dv[koff + (size_t)d] += ds * grow[d];"),
+    ("bwd_dq_from_v", "dqi[d] += scale * ds * load_elem(k, dtype, koff", "dqi[d] += scale * ds * load_elem(v, dtype, koff"),
+    ("bwd_unnormalised", "for (int64_t j = 0; j <= last; ++j) p[j] /= l;", ""),
+    ("bwd_causal_top_left", "const int64_t diag = i + ((int64_t)Sk - (int64_t)Sq);", "const int64_t diag = i;"),
+    ("bwd_dp_from_q", "dot += grow[d] * load_elem(v, dtype, voff", "dot += qrow[d] * load_elem(v, dtype, voff"),
 ]
 
 
