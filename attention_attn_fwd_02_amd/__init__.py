@@ -3,16 +3,17 @@
     from attention_attn_fwd_02_amd import fwd, fwd_decode
     o, lse = fwd(q, k, v, causal=True)          # prefill
     o, lse = fwd_decode(q1, k, v)               # few query rows: split-KV
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)   # gradients
 
 The library is loaded on first use (`attn.load_library`); importing the package
 does not touch the GPU.
 """
 from .attn import (ATTN_BF16, ATTN_FP16, ATTN_FP32, ATTN_OK, ATTN_ERR_INVALID_ARG,
-                   ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH, AttnError, attn_fwd,
-                   attn_fwd_decode, attn_fwd_decode_workspace, attn_status_str, fwd,
-                   fwd_decode, load_library)
+                   ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH, AttnError, attn_bwd,
+                   attn_bwd_workspace, attn_fwd, attn_fwd_decode, attn_fwd_decode_workspace,
+                   attn_status_str, bwd, fwd, fwd_decode, load_library)
 
 __all__ = ["ATTN_BF16", "ATTN_FP16", "ATTN_FP32", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
-           "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "AttnError", "attn_fwd",
-           "attn_fwd_decode", "attn_fwd_decode_workspace", "attn_status_str", "fwd",
-           "fwd_decode", "load_library"]
+           "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "AttnError", "attn_bwd",
+           "attn_bwd_workspace", "attn_fwd", "attn_fwd_decode", "attn_fwd_decode_workspace",
+           "attn_status_str", "bwd", "fwd", "fwd_decode", "load_library"]

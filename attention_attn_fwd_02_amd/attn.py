@@ -45,6 +45,11 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                     i32, vp, sz, vp]
     lib.attn_fwd_decode.restype = i32
+    lib.attn_bwd_workspace.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+    lib.attn_bwd_workspace.restype = i32
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                             i32, i32, vp, sz, vp]
+    lib.attn_bwd.restype = i32
     _lib = lib
     return lib
 
@@ -68,6 +73,21 @@ def attn_fwd_decode(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype
     return load_library().attn_fwd_decode(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
                                           int(causal), int(dtype), int(nsplit), workspace,
                                           int(workspace_bytes), stream)
+
+
+def attn_bwd_workspace(B, Hq, Sq):
+    """(status, bytes) of the C workspace query of the backward."""
+    n = ctypes.c_size_t(0)
+    st = load_library().attn_bwd_workspace(B, Hq, Sq, ctypes.byref(n))
+    return st, n.value
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype,
+             workspace, workspace_bytes, stream) -> int:
+    """The C entry point with raw integer pointers; returns the status code."""
+    return load_library().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D,
+                                   float(scale), int(causal), int(dtype), workspace,
+                                   int(workspace_bytes), stream)
 
 
 def attn_status_str(status: int) -> str:
@@ -151,3 +171,41 @@ def fwd_decode(q, k, v, causal=False, scale=None, nsplit=0, out=None, lse=None, 
     if st != ATTN_OK:
         raise AttnError(st)
     return out, (lse if want_lse else None)
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of `fwd` on torch device tensors (bf16 or fp16).
+
+    o and lse are `fwd`'s outputs for q, k, v; dout is the gradient of the loss
+    with respect to o.  The workspace (uint8 device tensor) is allocated here when
+    not given.
+    """
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _check_inputs(q, k, v)
+    if o.shape != q.shape or dout.shape != q.shape or o.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("o and dout must match q")
+    if lse is None or tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be the forward's [B, Hq, Sq] fp32 log-sum-exp")
+    if not (o.is_contiguous() and dout.is_contiguous() and lse.is_contiguous()):
+        raise ValueError("o, lse, dout must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st, need = attn_bwd_workspace(B, Hq, Sq)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                  dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                  B, Hq, Hkv, Sq, Sk, D, scale, causal, _dtype_code(q.dtype),
+                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                  stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return dq, dk, dv

@@ -188,6 +188,66 @@ extern "C" int attn_fwd_decode(const void* q, const void* k, const void* v, void
     return ATTN_OK;
 }
 
+extern "C" int attn_bwd_workspace(int B, int Hq, int Sq, size_t* bytes) {
+    if (!bytes || B < 1 || Hq < 1 || Sq < 1) return ATTN_ERR_INVALID_ARG;
+    if (!product_fits(B, Hq, Sq, 8)) return ATTN_ERR_INVALID_ARG;
+    *bytes = (size_t)2 * (size_t)B * (size_t)Hq * (size_t)Sq * sizeof(float);
+    return ATTN_OK;
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                        float scale, int causal, int dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    using namespace attn_impl;
+    int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    if (!lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return ATTN_ERR_INVALID_ARG;
+    if (dtype == ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+    const int64_t rows = (int64_t)B * Hq * Sq;
+    size_t need = 0;
+    if (attn_bwd_workspace(B, Hq, Sq, &need) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
+    const int64_t n_pre = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
+    const int64_t n_kv = (int64_t)B * Hkv * ((Sk + 127) / 128);
+    const int64_t n_q = (int64_t)B * Hq * ((Sq + 127) / 128);
+    if (n_pre > INT32_MAX || n_kv > INT32_MAX || n_q > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    const BwdKernels kf = select_bwd(dtype, D, causal ? 1 : 0);
+    if (!kf.pre || !kf.dkdv || !kf.dq) return ATTN_ERR_UNSUPPORTED;
+
+    BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.l2row = (float*)workspace;
+    p.drow = p.l2row + rows;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.c = (float)((double)scale * 1.4426950408889634);
+    p.scale = scale;
+    p.rows = rows;
+    void* args[] = {&p};
+    if (hipLaunchKernel(kf.pre, dim3((unsigned)n_pre), dim3(256), args, 0, stream) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    if (hipLaunchKernel(kf.dkdv, dim3((unsigned)n_kv), dim3(256), args, 0, stream) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    if (hipLaunchKernel(kf.dq, dim3((unsigned)n_q), dim3(256), args, 0, stream) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    return ATTN_OK;
+}
+
 extern "C" const char* attn_status_str(int status) {
     switch (status) {
     case ATTN_OK: return "ok";

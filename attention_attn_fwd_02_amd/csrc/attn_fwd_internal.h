@@ -58,6 +58,27 @@ struct MergeParams {
     int nsplit;
 };
 
+// Gradients: workspace rows of D_i = dO_i.O_i and LSE_i log2(e), then dK/dV and dQ.
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;   // the forward's natural-log LSE, [B*Hq*Sq]
+    void* dq;
+    void* dk;
+    void* dv;
+    float* l2row;       // workspace: LSE * log2(e) per query row
+    float* drow;        // workspace: dO . O per query row
+    int B, Hq, Hkv, Sq, Sk;
+    float c;            // scale * log2(e) (any sign)
+    float scale;
+    int64_t rows;       // B*Hq*Sq
+};
+struct BwdKernels { const void* pre; const void* dkdv; const void* dq; };
+BwdKernels select_bwd(int dtype, int D, int causal);   // null members: unsupported
+
 const void* select_decode_split(int dtype, int D, int causal);   // null: unsupported
 const void* select_decode_merge(int dtype, int D);
 

@@ -134,13 +134,36 @@ DECODE = {
 }
 
 
+# Training (FIBER page, evaluation set-up: FlashAttention backward with
+# L_context = 4096 and d_head = 128): the gradients of the headline forward.  The
+# output gradient dO is drawn after Q, K, V from the same generator, N(0, 1).
+BACKWARD = {
+    w.name: w for w in [
+        Workload("bwd_causal_bf16_b2_h32_s4096_d128", "bf16", 2, 32, 32, 4096, 4096, 128, True,
+                 1011, note="backward of the headline forward"),
+    ]
+}
+
+
+def make_dout(w: Workload, q):
+    """dO for a backward workload: N(0, 1) in the storage dtype, drawn after Q, K, V."""
+    g = torch.Generator().manual_seed(w.seed + 7919)
+    return torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype)
+
+
+def bwd_flops(w: Workload) -> int:
+    """Algorithmic backward FLOPs: five products of 2*D FLOPs per visible pair
+    (S recomputed, dV, dP, dQ, dK)."""
+    return 10 * w.D * w.visible_pairs()
+
+
 def lookup(name: str) -> Workload:
-    """A named workload, attention variant or decode workload."""
-    for table in (WORKLOADS, VARIANTS, DECODE):
+    """A named workload, attention variant, decode or backward workload."""
+    for table in (WORKLOADS, VARIANTS, DECODE, BACKWARD):
         if name in table:
             return table[name]
     raise KeyError("unknown workload %r (known: %s)" % (
-        name, ", ".join(list(WORKLOADS) + list(VARIANTS) + list(DECODE))))
+        name, ", ".join(list(WORKLOADS) + list(VARIANTS) + list(DECODE) + list(BACKWARD))))
 
 
 def _draw(g, shape, dist):

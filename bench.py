@@ -167,7 +167,7 @@ def main():
         copy_calibration(args.copy_mib, max(1, args.steps))
         return
 
-    from attention_attn_fwd_02_amd import fwd, fwd_decode, load_library
+    from attention_attn_fwd_02_amd import bwd, fwd, fwd_decode, load_library
     from attention_attn_fwd_02_amd import workloads as W
     load_library()
     name = args.workload or W.HEADLINE
@@ -182,7 +182,20 @@ def main():
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     decode = name in W.DECODE
-    if decode:
+    backward = name in W.BACKWARD
+    if backward:
+        # gradients of the forward; its O and LSE are computed once, outside the timing
+        from attention_attn_fwd_02_amd import attn_bwd_workspace
+        dod = W.make_dout(w, q).to(dev)
+        fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        st, nbytes = attn_bwd_workspace(w.B, w.Hq, w.Sq)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+
+        def step():
+            bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                workspace=ws, stream=stream)
+    elif decode:
         # split-KV pass + merge; the workspace is allocated once, outside the timing
         from attention_attn_fwd_02_amd import attn_fwd_decode_workspace
         st, nbytes = attn_fwd_decode_workspace(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, 0)
@@ -212,7 +225,7 @@ def main():
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / args.steps
     kern_ms = ev0.elapsed_time(ev1) / args.steps
-    flops = w.flops()
+    flops = W.bwd_flops(w) if backward else w.flops()
     value = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -224,12 +237,15 @@ def main():
         return
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not backward:
         cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
         log("cpu baseline: %.4g TFLOP/s on %d threads" % (cpu["value"], cpu["cores"]))
 
+    metric = "attention fwd TFLOP/s (bf16, causal S=4096 D=128) + % of MFMA peak"
+    if backward:
+        metric = "attention bwd TFLOP/s (bf16, causal S=4096 D=128, 10*D FLOP per pair) + % of MFMA peak"
     line = {
-        "metric": "attention fwd TFLOP/s (bf16, causal S=4096 D=128) + % of MFMA peak",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -136,6 +136,43 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int causal, int dtype, int nsplit,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Gradients of attn_fwd (the FlashAttention backward the FIBER page evaluates as
+ * its training workload: evaluation set-up, "Workloads"; results, "Decoding and
+ * Training Workloads Speedup").  For an output gradient dO and the weights
+ * P_ij = exp(scale q_i.k_j - LSE_i) over visible pairs,
+ *     dV = P^T dO,  dS = P o (dO V^T - rowsum(dO o O)),  dQ = scale dS K,
+ *     dK = scale dS^T Q,
+ * with the dK and dV of a key/value head summed over the query heads that read it.
+ *
+ * attn_bwd_workspace -- device workspace bytes attn_bwd needs (two fp32 values per
+ * query row); ATTN_ERR_INVALID_ARG for a null `bytes`, a size < 1 or overflowing
+ * sizes.
+ *
+ * attn_bwd -- enqueue the three kernels on `stream`.
+ *   q, k, v, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype: as given to attn_fwd
+ *   o      [B][Hq][Sq][D]  attn_fwd's output for these inputs
+ *   lse    [B][Hq][Sq]     attn_fwd's log-sum-exp (fp32, required here)
+ *   dout   [B][Hq][Sq][D]  gradient of the loss with respect to o
+ *   dq     [B][Hq][Sq][D]  output; dk, dv [B][Hkv][Sk][D] outputs; all fully written,
+ *                          element type `dtype`, 16-byte aligned, not overlapping
+ *                          any input
+ *   workspace, workspace_bytes: caller-owned device memory of at least the size
+ *                          attn_bwd_workspace reports, 16-byte aligned
+ * dtype must be ATTN_BF16 or ATTN_FP16 (ATTN_FP32: ATTN_ERR_UNSUPPORTED).  Errors
+ * are those of attn_fwd, plus ATTN_ERR_INVALID_ARG for a null lse, dout, dq, dk or
+ * dv, a misaligned pointer, or a missing or short workspace.  Gradients accumulate
+ * in fp32 and are rounded once; P and dS are rounded to `dtype` before they
+ * multiply Q, K or dO.  Deterministic: no atomics, fixed summation order.  Keys
+ * that no query sees get dK = dV = 0.
+ */
+int attn_bwd_workspace(int B, int Hq, int Sq, size_t* bytes);
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D,
+             float scale, int causal, int dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a return code ("unknown status" otherwise). */
 const char* attn_status_str(int status);
 

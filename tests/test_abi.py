@@ -36,7 +36,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"attn_fwd", "attn_status_str", "attn_fwd_decode",
-                          "attn_fwd_decode_workspace"}, names
+                          "attn_fwd_decode_workspace", "attn_bwd", "attn_bwd_workspace"}, names
     raw = ctypes.CDLL(A.LIB_PATH)
     for nm in names:
         assert hasattr(raw, nm), nm
@@ -189,3 +189,45 @@ def test_decode_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         A.fwd_decode(q, q, q)
+
+
+
+# ---- backward entry points (every call below fails validation) ----
+DO_, DQ_, DK_, DV_ = 0x70000, 0x80000, 0x90000, 0xA0000
+BGOOD = dict(q=Q, k=K, v=V, o=O, lse=L, do=DO_, dq=DQ_, dk=DK_, dv=DV_, B=1, Hq=4, Hkv=2, Sq=64,
+             Sk=64, D=128, scale=0.125, causal=1, dtype=A.ATTN_BF16, ws=W_ADDR, ws_bytes=1 << 20,
+             stream=None)
+
+
+def _bcall(**kw):
+    a = dict(BGOOD)
+    a.update(kw)
+    return A.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                      a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], a["scale"], a["causal"],
+                      a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_bwd_workspace_size(lib):
+    assert A.attn_bwd_workspace(2, 8, 100) == (A.ATTN_OK, 2 * 2 * 8 * 100 * 4)
+    assert A.attn_bwd_workspace(0, 8, 100)[0] == A.ATTN_ERR_INVALID_ARG
+    assert A.load_library().attn_bwd_workspace(1, 1, 1, None) == A.ATTN_ERR_INVALID_ARG
+
+
+BINVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(do=None),
+    dict(dq=None), dict(dk=None), dict(dv=None), dict(do=DO_ + 8), dict(dq=DQ_ + 2),
+    dict(dk=DK_ + 4), dict(dv=DV_ + 1), dict(lse=L + 2), dict(Hq=3, Hkv=2), dict(Sk=0),
+    dict(scale=float("inf")), dict(dtype=5), dict(ws=None), dict(ws=W_ADDR + 4),
+    dict(ws_bytes=64 * 4 * 8 - 1),
+]
+
+
+@pytest.mark.parametrize("bad", BINVALID, ids=[str(b) for b in BINVALID])
+def test_bwd_invalid_arguments(lib, bad):
+    assert _bcall(**bad) == A.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(dtype=A.ATTN_FP32), dict(D=96), dict(D=256)],
+                         ids=["fp32", "d96", "d256"])
+def test_bwd_unsupported(lib, bad):
+    assert _bcall(**bad) == A.ATTN_ERR_UNSUPPORTED
