@@ -145,6 +145,30 @@ BACKWARD = {
 }
 
 
+# Rotary position embedding ahead of attention (FIBER page, background and evaluation
+# set-up: RoPE is one of the vector operations modelled between the GEMMs; VDCores
+# page, evaluation: QKV projection fused with RoPE): the headline shape with Q and K
+# rotated as they are loaded.  The cos/sin tables are inputs, built by
+# `rope_tables` (the rotary embedding's frequencies with base 10000).
+ROPE = {
+    w.name: w for w in [
+        Workload("rope_causal_bf16_b2_h32_s4096_d128", "bf16", 2, 32, 32, 4096, 4096, 128, True,
+                 1012, note="headline shape, rotary embedding on Q and K (interleaved pairs)"),
+    ]
+}
+ROPE_LAYOUT = {"rope_causal_bf16_b2_h32_s4096_d128": 1}
+
+
+def rope_tables(P: int, D: int, base: float = 10000.0):
+    """cos/sin tables [P, D/2] (fp32) of the rotary embedding's angles:
+    position p, pair i turns by p * base^(-2i/D).  Angles and their cosines and
+    sines are taken in fp64 and rounded once to fp32."""
+    pos = torch.arange(P, dtype=torch.float64)[:, None]
+    inv = base ** (-torch.arange(D // 2, dtype=torch.float64) * 2.0 / D)
+    ang = pos * inv[None, :]
+    return torch.cos(ang).to(torch.float32).contiguous(), torch.sin(ang).to(torch.float32).contiguous()
+
+
 def make_dout(w: Workload, q):
     """dO for a backward workload: N(0, 1) in the storage dtype, drawn after Q, K, V."""
     g = torch.Generator().manual_seed(w.seed + 7919)
@@ -158,12 +182,13 @@ def bwd_flops(w: Workload) -> int:
 
 
 def lookup(name: str) -> Workload:
-    """A named workload, attention variant, decode or backward workload."""
-    for table in (WORKLOADS, VARIANTS, DECODE, BACKWARD):
+    """A named workload, attention variant, decode, backward or RoPE workload."""
+    for table in (WORKLOADS, VARIANTS, DECODE, BACKWARD, ROPE):
         if name in table:
             return table[name]
     raise KeyError("unknown workload %r (known: %s)" % (
-        name, ", ".join(list(WORKLOADS) + list(VARIANTS) + list(DECODE) + list(BACKWARD))))
+        name, ", ".join(list(WORKLOADS) + list(VARIANTS) + list(DECODE) + list(BACKWARD)
+                        + list(ROPE))))
 
 
 def _draw(g, shape, dist):

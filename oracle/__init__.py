@@ -7,7 +7,9 @@ Python binding) never imports it, and this package imports nothing from the
 product.
 
 The arithmetic lives in `attn_oracle.c` (plain C, fp64, two-pass softmax per
-row); this module only marshals arrays into it.  What it computes: the
+row; the rotary embedding of Q and K with one rounding into the storage type);
+this module only marshals arrays into it (and, for attention with the rotary
+embedding, chains the rotation into the forward).  What it computes: the
 multi-head scaled dot-product attention of Equ. 1 on the page "A
 Thread-Register Decoupled GPU Execution Model for Efficient Tensor Computation"
 (introduction), with the readings listed at the top of `attn_oracle.c`.
@@ -70,6 +72,10 @@ class OracleLib:
         lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f64,
                                         i32, vp, vp, vp, i32]
         lib.oracle_attn_bwd.restype = i32
+        lib.oracle_round16.argtypes = [vp, i32, i64, vp]
+        lib.oracle_round16.restype = i32
+        lib.oracle_rope.argtypes = [vp, i32, i64, i32, i32, vp, vp, i32, i32, i32, vp, vp]
+        lib.oracle_rope.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         self.lib = lib
@@ -84,6 +90,53 @@ class OracleLib:
         if rc:
             raise ValueError("oracle_widen failed (%d)" % rc)
         return out
+
+    def round16(self, x, dtype: str) -> np.ndarray:
+        """Round an fp64 array to bf16/fp16 (nearest, ties to even); returns the
+        storage bit patterns as uint16, same shape."""
+        src = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+        out = np.empty(src.shape, dtype=np.uint16)
+        rc = self.lib.oracle_round16(src.ctypes.data, _DTYPE_CODE[dtype], src.size, out.ctypes.data)
+        if rc:
+            raise ValueError("oracle_round16 failed (%d)" % rc)
+        return out
+
+    def rope(self, x, cos, sin, layout, pos_offset=0):
+        """Rotary embedding of x ([..., S, D], bf16 or fp16) with fp32 tables
+        cos, sin ([P, D/2]); row s of each head at position s + pos_offset.
+        layout 1: pairs (2i, 2i+1); layout 2: pairs (i, i + D/2).
+        Returns (fp64 rotated values, storage-typed rotated tensor)."""
+        import torch
+        xr, xn = _as_raw(x)
+        if xn not in ("bf16", "fp16"):
+            raise TypeError("oracle: rope takes bf16 or fp16")
+        S, D = xr.shape[-2], xr.shape[-1]
+        nheads = int(np.prod(xr.shape[:-2])) if xr.ndim > 2 else 1
+        ct = np.ascontiguousarray(np.asarray(cos, dtype=np.float32))
+        st = np.ascontiguousarray(np.asarray(sin, dtype=np.float32))
+        if ct.shape != st.shape or ct.ndim != 2 or ct.shape[1] != D // 2:
+            raise ValueError("oracle: rope tables must be [P, D/2]")
+        f64 = np.empty(xr.shape, dtype=np.float64)
+        bits = np.empty(xr.shape, dtype=np.uint16)
+        rc = self.lib.oracle_rope(xr.ctypes.data, _DTYPE_CODE[xn], nheads, S, D, ct.ctypes.data,
+                                  st.ctypes.data, ct.shape[0], int(pos_offset), int(layout),
+                                  f64.ctypes.data, bits.ctypes.data)
+        if rc:
+            raise ValueError("oracle_rope failed (%d)" % rc)
+        tdt = torch.bfloat16 if xn == "bf16" else torch.float16
+        return f64, torch.from_numpy(bits.view(np.int16)).view(tdt)
+
+    def attn_fwd_rope(self, q, k, v, cos, sin, layout, causal=False, scale=None, rows=None,
+                      nthreads=0):
+        """Attention of the rotated, storage-rounded Q and K: query i at position
+        i + Sk - Sq, key j at position j.  Returns (o, lse, k_rot) with o, lse as
+        `attn_fwd` and k_rot the rotated K in the storage type."""
+        Sq, Sk = q.shape[2], k.shape[2]
+        _, q_rot = self.rope(q, cos, sin, layout, pos_offset=Sk - Sq)
+        _, k_rot = self.rope(k, cos, sin, layout, pos_offset=0)
+        o, lse = self.attn_fwd(q_rot, k_rot, v, causal=causal, scale=scale, rows=rows,
+                               nthreads=nthreads)
+        return o, lse, k_rot
 
     def max_threads(self) -> int:
         return int(self.lib.oracle_max_threads())
@@ -178,6 +231,19 @@ def attn_fwd(q, k, v, causal=False, scale=None, rows=None, nthreads=0):
 
 def attn_bwd(q, k, v, do, causal=False, scale=None, nthreads=0):
     return default().attn_bwd(q, k, v, do, causal=causal, scale=scale, nthreads=nthreads)
+
+
+def round16(x, dtype):
+    return default().round16(x, dtype)
+
+
+def rope(x, cos, sin, layout, pos_offset=0):
+    return default().rope(x, cos, sin, layout, pos_offset=pos_offset)
+
+
+def attn_fwd_rope(q, k, v, cos, sin, layout, causal=False, scale=None, rows=None, nthreads=0):
+    return default().attn_fwd_rope(q, k, v, cos, sin, layout, causal=causal, scale=scale,
+                                   rows=rows, nthreads=nthreads)
 
 
 def widen(x) -> np.ndarray:

@@ -35,8 +35,10 @@
  *
  * Parity status: every function here is pinned by the CPU tests (closed forms,
  * invariants, 50-digit brute force on tiny inputs, an independent library
- * routine; the gradients also by central differences of the forward); the pages
- * print no attention values to pin against.
+ * routine; the gradients also by central differences of the forward; the rotary
+ * embedding by complex multiplication, exact rotations, the relative-position
+ * property and independent roundings); the pages print no attention values to
+ * pin against.
  */
 #include <math.h>
 #include <stddef.h>
@@ -301,6 +303,118 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dou
         free(dp);
     }
     return bad ? 2 : 0;
+}
+
+/* ---- Rotary position embedding (RoPE) -------------------------------------
+ *
+ * The FIBER page names RoPE among the vector operations that sit between the
+ * GEMMs of a transformer block (background; evaluation set-up, "Workloads"),
+ * and the VDCores page evaluates QKV projection fused with RoPE (evaluation,
+ * "dynamic fusion", Fig. 12).  Neither page writes the rotation out; it is read
+ * as the rotary embedding of the RoPE paper the FIBER page cites: the D features
+ * of a row form D/2 pairs, and pair i of the row at position p is turned through
+ * an angle whose cosine and sine the caller tabulates as cos_tab[p][i] and
+ * sin_tab[p][i]:
+ *
+ *     a' = a * c - b * s,      b' = a * s + b * c.
+ *
+ * Pairs are features (2i, 2i+1) (layout 1, the RoPE paper's arrangement) or
+ * (i, i + D/2) (layout 2, the split-halves arrangement).  Row s of a head sits at
+ * position s + pos_offset.  Each rotated value is computed in fp64 (both products
+ * are exact there for 16-bit inputs and fp32 table entries, so only the
+ * difference or sum rounds) and is then rounded once, to nearest with ties to
+ * even, into the storage type: the same result a separate RoPE step writing
+ * 16-bit tensors would give. */
+
+/* Round v to the nearest value of a binary format with `mant` fraction bits and
+ * normal exponents emin..emax (ties to an even last fraction bit), from the
+ * format's definition: below 2^emin the spacing is fixed at 2^(emin - mant)
+ * (subnormals); at or beyond 2^(emax + 1) after rounding the result is infinite. */
+static double round_to_format(double v, int mant, int emin, int emax) {
+    if (v != v || v == 0.0 || isinf(v)) return v;
+    int e;
+    (void)frexp(fabs(v), &e);          /* |v| = f * 2^e, f in [0.5, 1): exponent e - 1 */
+    int ex = e - 1;
+    if (ex < emin) ex = emin;
+    const double quantum = ldexp(1.0, ex - mant);
+    const double scaled = v / quantum;  /* exact: division by a power of two */
+    double r = floor(scaled);
+    const double frac = scaled - r;     /* exact: scaled has at most 53 bits */
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    const double out = copysign(r * quantum, v);   /* a value rounded to zero keeps its sign */
+    if (fabs(out) >= ldexp(1.0, emax + 1)) return v > 0 ? INFINITY : -INFINITY;
+    return out;
+}
+
+/* Encode a value already representable in the storage type as its bit pattern. */
+static uint16_t encode16(double r, int dtype) {
+    if (dtype == ORACLE_BF16) {
+        const float f = (float)r;       /* exact: every bf16 value is a binary32 value */
+        uint32_t w;
+        memcpy(&w, &f, sizeof w);
+        if (r != r) return 0x7fc0;
+        return (uint16_t)(w >> 16);
+    }
+    /* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits */
+    uint16_t sign = signbit(r) ? 0x8000 : 0;
+    double a = fabs(r);
+    if (r != r) return 0x7e00;
+    if (isinf(a)) return sign | 0x7c00;
+    if (a < ldexp(1.0, -14))            /* subnormal or zero: a = frac * 2^-24 */
+        return sign | (uint16_t)(a * ldexp(1.0, 24));
+    int e = ilogb(a);
+    uint16_t frac = (uint16_t)((ldexp(a, -e) - 1.0) * 1024.0);
+    return sign | (uint16_t)((e + 15) << 10) | frac;
+}
+
+static double round_to_storage(double v, int dtype) {
+    return dtype == ORACLE_BF16 ? round_to_format(v, 7, -126, 127)
+                                : round_to_format(v, 10, -14, 15);
+}
+
+/* Round n fp64 values to the 16-bit storage type (test helper for the pins). */
+int oracle_round16(const double* src, int dtype, int64_t n, uint16_t* dst) {
+    if (!src || !dst || n < 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_FP16)) return 1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = encode16(round_to_storage(src[i], dtype), dtype);
+    return 0;
+}
+
+/* Rotate every row of x ([nheads][S][D], 16-bit storage type) by the tabulated
+ * angles of its position; writes the unrounded fp64 result (may be NULL) and the
+ * rounded storage bits (may be NULL).  Tables are [ntab][D/2] fp32; a position
+ * outside 0..ntab-1 is an error. */
+int oracle_rope(const void* x, int dtype, int64_t nheads, int S, int D,
+                const float* cos_tab, const float* sin_tab, int ntab, int pos_offset,
+                int layout, double* out_f64, uint16_t* out_bits) {
+    if (!x || !cos_tab || !sin_tab || nheads < 0 || S < 0 || D < 2 || D % 2)
+        return 1;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return 1;
+    if (layout != 1 && layout != 2) return 1;
+    if (S > 0 && (pos_offset < 0 || pos_offset + S - 1 >= ntab)) return 2;
+    const int half = D / 2;
+    for (int64_t hs = 0; hs < nheads * (int64_t)S; ++hs) {
+        const int pos = (int)(hs % S) + pos_offset;
+        const size_t row = (size_t)hs * (size_t)D;
+        for (int i = 0; i < half; ++i) {
+            const int ia = layout == 1 ? 2 * i : i;
+            const int ib = layout == 1 ? 2 * i + 1 : i + half;
+            const double a = load_elem(x, dtype, row + (size_t)ia);
+            const double b = load_elem(x, dtype, row + (size_t)ib);
+            const double c = (double)cos_tab[(size_t)pos * half + i];
+            const double sn = (double)sin_tab[(size_t)pos * half + i];
+            const double ra = a * c - b * sn;
+            const double rb = a * sn + b * c;
+            if (out_f64) {
+                out_f64[row + (size_t)ia] = ra;
+                out_f64[row + (size_t)ib] = rb;
+            }
+            if (out_bits) {
+                out_bits[row + (size_t)ia] = encode16(round_to_storage(ra, dtype), dtype);
+                out_bits[row + (size_t)ib] = encode16(round_to_storage(rb, dtype), dtype);
+            }
+        }
+    }
+    return 0;
 }
 
 /* Number of threads an OpenMP parallel region here would use. */

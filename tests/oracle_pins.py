@@ -465,6 +465,159 @@ def pin_bwd_torch_autograd(orc):
             assert np.allclose(mine, ref.numpy(), rtol=0, atol=1e-11), (B, Hq, Hkv, Sq, Sk)
 
 
+# ----------------------------------------------------------------------------
+# 8. Rotary position embedding.  The rotation of a feature pair by a tabulated
+#    (cos, sin) is the product of two complex numbers; the rounding into the
+#    storage type is checked against independent roundings; the rotation's
+#    defining property -- dot products of rotated rows depend only on the
+#    difference of their positions -- is checked on unrounded values.
+# ----------------------------------------------------------------------------
+def _angles_tables(P, D, base=10000.0):
+    ang = np.arange(P, dtype=np.float64)[:, None] * base ** (-np.arange(D // 2) * 2.0 / D)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _interleave_perm(D):
+    """perm[j] = feature of the split-halves layout that sits at feature j of the
+    interleaved layout: pair i is (i, i + D/2) there and (2i, 2i+1) here."""
+    half = D // 2
+    perm = np.empty(D, dtype=np.int64)
+    perm[0::2] = np.arange(half)
+    perm[1::2] = np.arange(half) + half
+    return perm
+
+
+def pin_rope_complex_product(orc):
+    """Interleaved pairs (a, b) at position p become (a + ib)(c_p + i s_p) exactly
+    (the products are exact in fp64); the split-halves layout is the interleaved
+    one on permuted features; row s of a head reads table row s + pos_offset."""
+    g = torch.Generator().manual_seed(801)
+    rng = _rng(802)
+    for dt in (torch.bfloat16, torch.float16):
+        B, H, S, D, off = 2, 3, 7, 8, 5
+        x = torch.randn(B, H, S, D, generator=g).to(dt)
+        # arbitrary (not unit) tables make every entry count
+        ct = rng.standard_normal((S + off + 2, D // 2)).astype(np.float32)
+        st = rng.standard_normal((S + off + 2, D // 2)).astype(np.float32)
+        f1, t1 = orc.rope(x, ct, st, 1, pos_offset=off)
+        xd = x.double().numpy()
+        z = (xd[..., 0::2] + 1j * xd[..., 1::2]) * (ct[off:off + S].astype(np.float64)
+                                                    + 1j * st[off:off + S].astype(np.float64))
+        assert np.array_equal(f1[..., 0::2], z.real) and np.array_equal(f1[..., 1::2], z.imag), dt
+        # the storage output is the fp64 result rounded once
+        name = "bf16" if dt == torch.bfloat16 else "fp16"
+        assert np.array_equal(t1.view(torch.int16).numpy().view(np.uint16), orc.round16(f1, name)), dt
+        perm = _interleave_perm(D)
+        f2, t2 = orc.rope(x, ct, st, 2, pos_offset=off)
+        fp, tp = orc.rope(x[..., perm].contiguous(), ct, st, 1, pos_offset=off)
+        inv = np.argsort(perm)
+        assert np.array_equal(f2, fp[..., inv]), dt
+        assert torch.equal(t2.view(torch.int16), tp[..., inv].contiguous().view(torch.int16)), dt
+
+
+def pin_rope_exact_rotations(orc):
+    """Angle 0 is the identity, a quarter turn maps (a, b) to (-b, a) and a half
+    turn negates: all exact, in both layouts, after rounding."""
+    g = torch.Generator().manual_seed(803)
+    for dt in (torch.bfloat16, torch.float16):
+        x = torch.randn(1, 2, 4, 16, generator=g).to(dt)
+        P = 4
+        ones, zeros = np.ones((P, 8), np.float32), np.zeros((P, 8), np.float32)
+        for layout in (1, 2):
+            perm = _interleave_perm(16) if layout == 2 else np.arange(16)
+            _, t = orc.rope(x, ones, zeros, layout)
+            assert torch.equal(t.view(torch.int16), x.view(torch.int16)), (dt, layout)
+            _, t = orc.rope(x, -ones, zeros, layout)
+            assert torch.equal(t.double(), -x.double()), (dt, layout)
+            _, t = orc.rope(x, zeros, ones, layout)
+            xp, tp = x[..., perm].double(), t[..., perm].double()
+            assert torch.equal(tp[..., 0::2], -xp[..., 1::2]), (dt, layout)
+            assert torch.equal(tp[..., 1::2], xp[..., 0::2]), (dt, layout)
+
+
+def pin_rope_relative_position(orc):
+    """With the frequency tables of the rotary embedding, the dot product of a
+    query rotated at position m with a key rotated at position n depends only on
+    m - n, and rotation keeps each row's norm (up to the fp32 tables' rounding)."""
+    g = torch.Generator().manual_seed(804)
+    D, P = 64, 300
+    ct, st = _angles_tables(P, D)
+    q = torch.randn(1, 1, 1, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 1, 1, D, generator=g).to(torch.bfloat16)
+    for layout in (1, 2):
+        def dot(m, n):
+            fq, _ = orc.rope(q, ct, st, layout, pos_offset=m)
+            fk, _ = orc.rope(k, ct, st, layout, pos_offset=n)
+            return float((fq * fk).sum())
+        for m, n, t in ((3, 1, 100), (50, 70, 200), (0, 0, 299), (200, 10, 50)):
+            a, b = dot(m, n), dot(m + t, n + t)
+            assert abs(a - b) <= 1e-5 * (1 + abs(a)), (layout, m, n, t, a, b)
+        assert abs(dot(7, 0) - dot(0, 7)) > 1e-3      # the sign of m - n matters
+        fq, _ = orc.rope(q, ct, st, layout, pos_offset=123)
+        nq = float((q.double() ** 2).sum())
+        assert abs(float((fq ** 2).sum()) - nq) <= 1e-6 * nq, layout
+
+
+def _nearest_even_bf16(v):
+    """Nearest bf16 to v (ties to an even bit pattern) by searching the bit
+    patterns around v's binary32 rounding, decoding each one exactly."""
+    f = np.array([v], dtype=np.float64).astype(np.float32)
+    top = int(f.view(np.uint32)[0]) >> 16
+    best = None
+    for cand in range(max(0, (top & 0x7fff) - 2), (top & 0x7fff) + 3):
+        for c in (cand, cand | 0x8000):
+            val = float(np.array([c << 16], dtype=np.uint32).view(np.float32)[0])
+            if not math.isfinite(val):
+                continue
+            # nearest, then an even last bit, then the sign of v for zeros
+            key = (abs(val - v), c & 1, (c >> 15) != (1 if math.copysign(1.0, v) < 0 else 0))
+            if best is None or key < best[0]:
+                best = (key, c)
+    return best[1]
+
+
+def pin_round16(orc):
+    """Rounding fp64 into the storage types: fp16 agrees with numpy's correctly
+    rounded float64 -> float16 conversion (normal, subnormal, ties, overflow);
+    bf16 agrees with a nearest-even search over decoded neighbours."""
+    rng = _rng(805)
+    ulp_ties = np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2.0 ** -24 * 0.5, 2.0 ** -24 * 1.5,
+                         65504.0 + 16.0, 65504.0 + 15.9, -(1.0 + 2.0 ** -11), 2.0 ** -14 * (1 - 2.0 ** -11)])
+    x = np.concatenate([rng.standard_normal(20000) * 3, rng.standard_normal(2000) * 1e-6,
+                        rng.standard_normal(2000) * 3e4, ulp_ties, [0.0, -0.0, 1e6, -1e6]])
+    got = orc.round16(x, "fp16")
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+    bt = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -40,
+                   -(1.0 + 2.0 ** -8), 3.0e-39, 2.0 ** -133 * 1.5, 2.0 ** -133 * 0.5])
+    xb = np.concatenate([rng.standard_normal(3000) * 5, rng.standard_normal(300) * 1e-38, bt])
+    got = orc.round16(xb, "bf16")
+    for v, gb in zip(xb, got):
+        assert int(gb) == _nearest_even_bf16(float(v)), (v, hex(int(gb)))
+
+
+def pin_rope_bottom_right(orc):
+    """Attention with the rotary embedding places query i at position
+    i + Sk - Sq: the last Sq query rows of a square causal problem give the same
+    outputs as the problem with only those queries."""
+    g = torch.Generator().manual_seed(806)
+    D, Sk, Sq = 16, 11, 3
+    ct, st = _angles_tables(Sk, D, base=50.0)
+    q = torch.randn(1, 2, Sk, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 1, Sk, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(1, 1, Sk, D, generator=g).to(torch.bfloat16)
+    for layout in (1, 2):
+        of, lf, kf = orc.attn_fwd_rope(q, k, v, ct, st, layout, causal=True)
+        qs = q[:, :, Sk - Sq:].contiguous()
+        os_, ls, ks = orc.attn_fwd_rope(qs, k, v, ct, st, layout, causal=True)
+        assert np.array_equal(os_, of[:, :, Sk - Sq:]) and np.array_equal(ls, lf[:, :, Sk - Sq:])
+        assert torch.equal(kf.view(torch.int16), ks.view(torch.int16))
+        # and it is attention of the rotated tensors: row 0 of the square problem
+        # sees key 0 only, whose rotation at position 0 is the identity
+        assert abs(lf[0, 0, 0] - float((q[0, 0, 0].double() * k[0, 0, 0].double()).sum()) / 4.0) < 1e-12
+
+
 ALL_PINS = [
     pin_bruteforce_decimal,
     pin_hand_examples,
@@ -483,4 +636,9 @@ ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_special_cases,
     pin_bwd_torch_autograd,
+    pin_rope_complex_product,
+    pin_rope_exact_rotations,
+    pin_rope_relative_position,
+    pin_round16,
+    pin_rope_bottom_right,
 ]

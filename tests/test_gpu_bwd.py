@@ -101,3 +101,35 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_bwd_full_size_sampled_heads():
+    """The backward workload at full size (B=2, H=32, S=4096, D=128, causal bf16),
+    run in the launch configuration the benchmark times; whole heads are checked
+    against the oracle run on that head alone (heads do not interact)."""
+    w = W.lookup("bwd_causal_bf16_b2_h32_s4096_d128")
+    dev = torch.device("cuda:0")
+    q, k, v = W.make_inputs(w)
+    do = W.make_dout(w, q)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fwd(qd, kd, vd, causal=True, scale=w.scale)
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    bwd(qd, kd, vd, o, lse, dod, causal=True, scale=w.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert not torch.isnan(t).any(), "NaN in a gradient (unwritten or invalid)"
+    heads = ((0, 0), (1, 31), (0, 17))
+    say("case", w.name, "heads", heads)
+    # the chosen heads stacked as a batch of one-head problems (one oracle thread each)
+    sl = lambda t: torch.cat([t[b:b + 1, h:h + 1] for b, h in heads]).contiguous()
+    ref = oracle.attn_bwd(sl(q), sl(k), sl(v), sl(do), causal=True, scale=w.scale)
+    for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        gf = sl(got.cpu()).to(torch.float64).numpy()
+        for i, bh in enumerate(heads):
+            err = float(np.abs(gf[i] - want[i]).max())
+            tol = bwd_tolerance(want[i], w.dtype)
+            say("  %s head %s: max|err| %.3g  max|ref| %.3g  tol %.3g"
+                % (name, bh, err, np.abs(want[i]).max(), tol))
+            assert err <= tol, "head %s %s: max |err| %.3g > %.3g" % (bh, name, err, tol)

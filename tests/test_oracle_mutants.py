@@ -44,6 +44,19 @@ MUTANTS = [
     ("bwd_unnormalised", "for (int64_t j = 0; j <= last; ++j) p[j] /= l;", ""),
     ("bwd_causal_top_left", "const int64_t diag = i + ((int64_t)Sk - (int64_t)Sq);", "const int64_t diag = i;"),
     ("bwd_dp_from_q", "dot += grow[d] * load_elem(v, dtype, voff", "dot += qrow[d] * load_elem(v, dtype, voff"),
+    ("rope_sin_sign", "const double ra = a * c - b * sn;", "const double ra = a * c + b * sn;"),
+    ("rope_second_of_pair", "const double rb = a * sn + b * c;", "const double rb = b * sn + a * c;"),
+    ("rope_pairs_adjacent_halves", "const int ib = layout == 1 ? 2 * i + 1 : i + half;",
+     "const int ib = layout == 1 ? 2 * i + 1 : i + 1;"),
+    ("rope_offset_dropped", "const int pos = (int)(hs % S) + pos_offset;", "const int pos = (int)(hs % S);"),
+    ("rope_frequency_shift", "const double c = (double)cos_tab[(size_t)pos * half + i];",
+     "const double c = (double)cos_tab[(size_t)pos * half + (i + 1) % half];"),
+    ("rope_sin_from_cos_table", "const double sn = (double)sin_tab[", "const double sn = (double)cos_tab["),
+    ("round_ties_away", "(frac == 0.5 && fmod(r, 2.0) != 0.0)", "(frac == 0.5)"),
+    ("round_truncates", "if (frac > 0.5 ||", "if (frac > 1.5 ||"),
+    ("round_subnormal_spacing", "if (ex < emin) ex = emin;", "if (ex < emin) ex = emin - 1;"),
+    ("round_bf16_fraction_bits", "round_to_format(v, 7, -126, 127)", "round_to_format(v, 8, -126, 127)"),
+    ("fp16_encode_subnormal", "(uint16_t)(a * ldexp(1.0, 24))", "(uint16_t)(a * ldexp(1.0, 23))"),
 ]
 
 

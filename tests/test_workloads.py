@@ -1,4 +1,6 @@
 """The seeded input generator and the FLOP convention (CPU only)."""
+import math
+
 import pytest
 import torch
 
@@ -65,3 +67,19 @@ def test_attention_variants():
     assert q.dtype == torch.float16 and k.shape == (1, 1, 8, 64)
     with pytest.raises(KeyError):
         W.lookup("no_such_workload")
+
+
+def test_rope_tables():
+    """Position 0 is the identity, pair 0 turns by one radian per position, the
+    last pair by base^(-(D-2)/D) radians, and every entry is a rounded unit vector."""
+    c, s = W.rope_tables(4096, 128)
+    assert c.shape == (4096, 64) and c.dtype == torch.float32
+    assert torch.all(c[0] == 1) and torch.all(s[0] == 0)
+    assert abs(float(c[3, 0]) - math.cos(3.0)) < 1e-7 and abs(float(s[3, 0]) - math.sin(3.0)) < 1e-7
+    theta = 10000.0 ** (-126.0 / 128.0)
+    assert abs(float(s[4000, 63]) - math.sin(4000 * theta)) < 1e-7
+    n = c.double() ** 2 + s.double() ** 2
+    assert float((n - 1).abs().max()) < 2e-7
+    w = W.lookup("rope_causal_bf16_b2_h32_s4096_d128")
+    assert (w.B, w.Hq, w.Sq, w.D, w.causal) == (2, 32, 4096, 128, True)
+    assert W.ROPE_LAYOUT[w.name] in (1, 2)
