@@ -1,7 +1,7 @@
 """Thin Python binding of the C-ABI library `libattn_fwd.so` (include/attn_fwd.h).
 
-Argument marshalling only: every step of the attention forward runs in the HIP
-kernels behind `attn_fwd` and `attn_fwd_decode`.  PyTorch supplies device memory and the stream.  If
+Argument marshalling only: every step runs in the HIP kernels behind `attn_fwd`,
+`attn_fwd_decode`, `attn_bwd` and `attn_fwd_rope`.  PyTorch supplies device memory and the stream.  If
 the library is missing this module raises; there is no fallback path.
 """
 import ctypes
@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(PKG, "libattn_fwd.so")
 
 # attn_dtype_t
 ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
+# attn_rope_layout_t
+ATTN_ROPE_INTERLEAVED, ATTN_ROPE_HALVES = 1, 2
 # attn_status_t
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
 
@@ -50,6 +52,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                              i32, i32, vp, sz, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                  f32, i32, i32, vp]
+    lib.attn_fwd_rope.restype = i32
     _lib = lib
     return lib
 
@@ -88,6 +93,14 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, scale, ca
     return load_library().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D,
                                    float(scale), int(causal), int(dtype), workspace,
                                    int(workspace_bytes), stream)
+
+
+def attn_fwd_rope(q, k, v, o, lse, k_rot, rope_cos, rope_sin, rope_layout, B, Hq, Hkv, Sq, Sk, D,
+                  scale, causal, dtype, stream) -> int:
+    """The C entry point with raw integer pointers; returns the status code."""
+    return load_library().attn_fwd_rope(q, k, v, o, lse, k_rot, rope_cos, rope_sin,
+                                        int(rope_layout), B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                        int(causal), int(dtype), stream)
 
 
 def attn_status_str(status: int) -> str:
@@ -209,3 +222,37 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=No
     if st != ATTN_OK:
         raise AttnError(st)
     return dq, dk, dv
+
+
+def fwd_rope(q, k, v, rope_cos, rope_sin, layout=ATTN_ROPE_INTERLEAVED, causal=False, scale=None,
+             out=None, lse=None, want_lse=True, k_rot=None, stream=None):
+    """Attention with the rotary embedding applied to Q and K (bf16 or fp16).
+
+    rope_cos, rope_sin: [P, D/2] fp32 device tables with P >= Sk (position p in
+    row p); key j sits at position j and query i at i + Sk - Sq (Sq <= Sk).
+    Returns (o, lse, k_rot): k_rot is the rotated K (allocated here unless given).
+    """
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _check_inputs(q, k, v)
+    for t in (rope_cos, rope_sin):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("rope tables must be contiguous fp32 device tensors")
+        if t.dim() != 2 or t.shape[1] != D // 2 or t.shape[0] < Sk:
+            raise ValueError("rope tables must be [P >= Sk, D/2]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if k_rot is None:
+        k_rot = torch.empty_like(k)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_fwd_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       lse.data_ptr() if want_lse else None, k_rot.data_ptr(),
+                       rope_cos.data_ptr(), rope_sin.data_ptr(), layout, B, Hq, Hkv, Sq, Sk, D,
+                       scale, causal, _dtype_code(q.dtype), stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, (lse if want_lse else None), k_rot

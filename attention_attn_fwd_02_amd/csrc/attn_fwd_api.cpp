@@ -78,19 +78,18 @@ size_t decode_workspace(int64_t rows, int D, int nsplit) {
     return (size_t)nsplit * (size_t)rows * ((size_t)D + 1) * sizeof(float);
 }
 
-}  // namespace
-
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int Hq, int Hkv, int Sq, int Sk, int D,
-                        float scale, int causal, int dtype, hipStream_t stream) {
+// Parameters and launch of the prefill kernel (arguments already validated).
+// rope: 0, or the rotary layout with its tables (then k is the rotated copy).
+int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+               int dtype, int rope, const float* rcos, const float* rsin, hipStream_t stream) {
     using namespace attn_impl;
-    const int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
-    if (st != ATTN_OK) return st;
-
-    const KernelChoice kc = select_kernel(dtype, D, causal ? 1 : 0);
+    const KernelChoice kc = select_kernel(dtype, D, causal ? 1 : 0, rope);
     if (!kc.fn) return ATTN_ERR_UNSUPPORTED;
 
     AttnParams p;
+    p.rcos = rcos;
+    p.rsin = rsin;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -121,6 +120,53 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     const hipError_t err = hipLaunchKernel(kc.fn, dim3((unsigned)nwg), dim3(kc.threads), args, 0,
                                            stream);
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                        float scale, int causal, int dtype, hipStream_t stream) {
+    const int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    return launch_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, 0, nullptr,
+                      nullptr, stream);
+}
+
+extern "C" int attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                             void* k_rot, const float* rope_cos, const float* rope_sin,
+                             int rope_layout, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                             float scale, int causal, int dtype, hipStream_t stream) {
+    using namespace attn_impl;
+    const int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    if (!k_rot || !rope_cos || !rope_sin) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(k_rot, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16))
+        return ATTN_ERR_INVALID_ARG;
+    if (rope_layout != ATTN_ROPE_INTERLEAVED && rope_layout != ATTN_ROPE_HALVES)
+        return ATTN_ERR_INVALID_ARG;
+    if (Sq > Sk) return ATTN_ERR_INVALID_ARG;
+    if (dtype == ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+    // the attention kernel addresses the tables with 32-bit byte offsets
+    if ((int64_t)Sk * (D / 2) * 4 > (INT64_C(1) << 31) - (INT64_C(1) << 20)) return ATTN_ERR_UNSUPPORTED;
+
+    const void* rk = select_rope(dtype, D, rope_layout);
+    if (!rk) return ATTN_ERR_UNSUPPORTED;
+    RopeParams rp;
+    rp.x = k;
+    rp.y = k_rot;
+    rp.rcos = rope_cos;
+    rp.rsin = rope_sin;
+    rp.rows = (int64_t)B * Hkv * Sk;
+    rp.S = Sk;
+    const int64_t threads = rp.rows * (D / 16);
+    const int64_t nblk = (threads + 255) / 256;
+    if (nblk > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    void* a1[] = {&rp};
+    if (hipLaunchKernel(rk, dim3((unsigned)nblk), dim3(256), a1, 0, stream) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    return launch_fwd(q, k_rot, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype,
+                      rope_layout, rope_cos, rope_sin, stream);
 }
 
 extern "C" int attn_fwd_decode_workspace(int B, int Hq, int Hkv, int Sq, int Sk, int D, int nsplit,

@@ -24,7 +24,20 @@ struct AttnParams {
     int nq;           // query tiles per head
     int xcd_remap;    // 1: give each XCD whole bundles of key/value-head groups
     int gbundle;      // key/value-head groups per bundle (divides B * Hkv)
+    const float* rcos;  // rotary embedding tables [Sk][D/2] (kernels built with it only)
+    const float* rsin;
 };
+
+// Rotary embedding of K into the rotated copy the attention then reads.
+struct RopeParams {
+    const void* x;      // [rows][D] 16-bit
+    void* y;            // [rows][D] 16-bit
+    const float* rcos;  // [S][D/2]
+    const float* rsin;
+    int64_t rows;       // B * H * S
+    int S;              // row r sits at position r % S
+};
+const void* select_rope(int dtype, int D, int layout);
 
 struct KernelChoice {
     const void* fn;   // __global__ function, or null when the combination is unsupported
@@ -32,7 +45,9 @@ struct KernelChoice {
     int threads;      // threads per workgroup
 };
 
-KernelChoice select_kernel(int dtype, int D, int causal);
+// rope: 0 none, 1 interleaved pairs (2i, 2i+1), 2 split halves (i, i + D/2); the
+// rotary variants exist for the 16-bit types only
+KernelChoice select_kernel(int dtype, int D, int causal, int rope = 0);
 
 // Split-KV pass for few query rows: one wave per (batch, K/V head, chunk).
 struct DecodeParams {

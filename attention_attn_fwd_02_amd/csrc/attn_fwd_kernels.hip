@@ -142,7 +142,7 @@ template <int D> struct Tile16 {
     static constexpr int VDMA_W = (VDMA + NW - 1) / NW;
 };
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int ROPE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_16(AttnParams p) {
     typedef Elem16<DT> E;
@@ -188,17 +188,65 @@ void attn_fwd_16(AttnParams p) {
     // ---- Q^T fragments (B operand): lane (n, h) holds Q[qw + n][16s + 8h .. +7];
     // rows past Sq read as zero
     vec8 qf[KSTEPS];
-    {
-        const uint32_t qx = (p.q_mode == 1) ? 0x80008000u : 0u;
-        const uint32_t qz = (p.q_mode == 2) ? 0u : 0xffffffffu;
+    const uint32_t qx = (p.q_mode == 1) ? 0x80008000u : 0u;
+    const uint32_t qz = (p.q_mode == 2) ? 0u : 0xffffffffu;
+    u32x4 raw[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        const uint32_t vo = (uint32_t)(qw + n) * T::ROW + (16 * s + 8 * h) * 2;
+        raw[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, vo, 0, 0));
+    }
+    // rotary embedding: query qi sits at position qi + Sk - Sq; the tables hold
+    // positions 0 .. Sk-1 and read as zero past them (rows past Sq, zero anyway).
+    // Interleaved pairs: dword e of fragment s is pair 8s + 4h + e, one 16-byte
+    // table load per fragment.  Split halves: element j of fragment s pairs with
+    // element j of fragment s + KSTEPS/2 as pair 16s + 8h + j, two table loads
+    // (entries 2s, 2s+1) per fragment pair.
+    u32x4 cv[KSTEPS], sv[KSTEPS];
+    if constexpr (ROPE != 0) {
+        constexpr int HALF = D / 2;
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.rcos, (uint32_t)p.Sk * HALF * 4);
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.rsin, (uint32_t)p.Sk * HALF * 4);
+        const uint32_t tab = (uint32_t)(qw + n + off) * (HALF * 4);
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const uint32_t vo = (uint32_t)(qw + n) * T::ROW + (16 * s + 8 * h) * 2;
-            u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, vo, 0, 0));
-            raw = (raw & qz) ^ qx;
-            qf[s] = __builtin_bit_cast(vec8, raw);
+            const uint32_t to = (ROPE == 1) ? tab + (8 * s + 4 * h) * 4
+                                            : tab + (16 * (s >> 1) + 8 * h) * 4 + 16 * (s & 1);
+            cv[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, to, 0, 0));
+            sv[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, to, 0, 0));
         }
     }
+    // the fragments as MFMA operands: rotated (rotary kernels; done once the first
+    // tiles' DMA is in flight, so it overlaps their latency), then the sign or zero
+    // of the scale applied
+    auto finish_q = [&]() {
+        if constexpr (ROPE == 1) {
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float ra, rb;
+                    rope_rotate(E::lo(raw[s][e]), E::hi(raw[s][e]), u2f(cv[s][e]), u2f(sv[s][e]), ra, rb);
+                    raw[s][e] = E::pack(ra, rb);
+                }
+        } else if constexpr (ROPE == 2) {
+#pragma unroll
+            for (int s = 0; s < KSTEPS / 2; ++s)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t wa = raw[s][e], wb = raw[s + KSTEPS / 2][e];
+                    const int t = 2 * s + (e >> 1), c0 = 2 * (e & 1);
+                    float ra0, rb0, ra1, rb1;
+                    rope_rotate(E::lo(wa), E::lo(wb), u2f(cv[t][c0]), u2f(sv[t][c0]), ra0, rb0);
+                    rope_rotate(E::hi(wa), E::hi(wb), u2f(cv[t][c0 + 1]), u2f(sv[t][c0 + 1]), ra1, rb1);
+                    raw[s][e] = E::pack(ra0, ra1);
+                    raw[s + KSTEPS / 2][e] = E::pack(rb0, rb1);
+                }
+        }
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(vec8, (raw[s] & qz) ^ qx);
+    };
+    if constexpr (ROPE == 0) finish_q();
 
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -397,6 +445,7 @@ void attn_fwd_16(AttnParams p) {
     dma_k(0, kbuf(0));
     dma_v(0, vbuf(0));
     dma_k(1, kbuf(1));
+    if constexpr (ROPE != 0) finish_q();
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
     if (0 < wkend && ntiles > 0) {
@@ -596,18 +645,24 @@ __global__ __launch_bounds__(256) void attn_fwd_32(AttnParams p) {
 // ---------------------------------------------------------------------------
 // kernel selection
 // ---------------------------------------------------------------------------
+template <int DT, int D, int ROPE>
+static const void* pick16r(int causal) {
+    return causal ? (const void*)&attn_fwd_16<DT, D, true, ROPE> : (const void*)&attn_fwd_16<DT, D, false, ROPE>;
+}
 template <int DT, int D>
-static const void* pick16(int causal) {
-    return causal ? (const void*)&attn_fwd_16<DT, D, true> : (const void*)&attn_fwd_16<DT, D, false>;
+static const void* pick16(int causal, int rope) {
+    return rope == 0 ? pick16r<DT, D, 0>(causal) : rope == 1 ? pick16r<DT, D, 1>(causal)
+         : rope == 2 ? pick16r<DT, D, 2>(causal) : nullptr;
 }
 template <int D>
 static const void* pick32(int causal) {
     return causal ? (const void*)&attn_fwd_32<D, true> : (const void*)&attn_fwd_32<D, false>;
 }
 
-KernelChoice select_kernel(int dtype, int D, int causal) {
+KernelChoice select_kernel(int dtype, int D, int causal, int rope) {
     KernelChoice kc = {nullptr, 0, 0};
     if (dtype == ATTN_IMPL_FP32) {
+        if (rope != 0) return kc;
         kc.bm = BM32;
         kc.threads = 256;
         kc.fn = (D == 64) ? pick32<64>(causal) : (D == 128) ? pick32<128>(causal) : nullptr;
@@ -616,11 +671,11 @@ KernelChoice select_kernel(int dtype, int D, int causal) {
     kc.bm = BM16;
     kc.threads = 64 * NW;
     if (dtype == ATTN_IMPL_BF16)
-        kc.fn = (D == 64) ? pick16<ATTN_IMPL_BF16, 64>(causal)
-              : (D == 128) ? pick16<ATTN_IMPL_BF16, 128>(causal) : nullptr;
+        kc.fn = (D == 64) ? pick16<ATTN_IMPL_BF16, 64>(causal, rope)
+              : (D == 128) ? pick16<ATTN_IMPL_BF16, 128>(causal, rope) : nullptr;
     else if (dtype == ATTN_IMPL_FP16)
-        kc.fn = (D == 64) ? pick16<ATTN_IMPL_FP16, 64>(causal)
-              : (D == 128) ? pick16<ATTN_IMPL_FP16, 128>(causal) : nullptr;
+        kc.fn = (D == 64) ? pick16<ATTN_IMPL_FP16, 64>(causal, rope)
+              : (D == 128) ? pick16<ATTN_IMPL_FP16, 128>(causal, rope) : nullptr;
     return kc;
 }
 

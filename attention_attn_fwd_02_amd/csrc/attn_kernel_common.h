@@ -1,6 +1,7 @@
 // attn_kernel_common.h -- device-side helpers shared by the attention kernels
-// (prefill and decode): vector types, wave-pair reductions, 16-bit element
-// traits and buffer resources.  Included by the .hip sources only.
+// (prefill, decode, backward, rotary embedding): vector types, wave-pair
+// reductions, 16-bit element traits, the rotation of a feature pair and buffer
+// resources.  Included by the .hip sources only.
 #ifndef ATTN_KERNEL_COMMON_H
 #define ATTN_KERNEL_COMMON_H
 
@@ -52,6 +53,9 @@ template <> struct Elem16<ATTN_IMPL_BF16> {
         bf16x2 v = {(__bf16)lo, (__bf16)hi};
         return __builtin_bit_cast(uint32_t, v);
     }
+    // the two elements of a packed dword, exactly, as fp32
+    static __device__ __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 };
 template <> struct Elem16<ATTN_IMPL_FP16> {
     typedef f16x8 vec8;
@@ -62,7 +66,52 @@ template <> struct Elem16<ATTN_IMPL_FP16> {
         f16x2 v = {(_Float16)lo, (_Float16)hi};
         return __builtin_bit_cast(uint32_t, v);
     }
+    static __device__ __forceinline__ float lo(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
 };
+
+// ---------------------------------------------------------------------------
+// rotary position embedding of one feature pair
+// ---------------------------------------------------------------------------
+
+// The bits of a dword as fp32.  The argument is taken by value on purpose: hipcc
+// compiles __builtin_bit_cast applied directly to an element of a vector value
+// (v[i]) into a read of element 0 (an element of a vector is not addressable), so
+// elements are always copied into a scalar first.
+__device__ __forceinline__ float u2f(uint32_t w) { return __builtin_bit_cast(float, w); }
+
+// fp64 -> fp32 with rounding to odd: truncate toward zero, then set the last
+// fraction bit when the truncation was inexact.  A following round-to-nearest-even
+// into a format with at least two fewer fraction bits (bf16, fp16) then equals one
+// direct rounding of the fp64 value (Boldo and Melquiond, "Emulation of FMA and
+// correctly rounded sums: proved algorithms using rounding to odd", IEEE
+// Transactions on Computers 57(4), 2008).
+__device__ __forceinline__ float round_odd_f32(double d) {
+    float f = (float)d;                         // nearest even
+    const double back = (double)f;
+    if (back != d) {
+        uint32_t u = __builtin_bit_cast(uint32_t, f);
+        if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1u;   // one step toward zero
+        u |= 1u;
+        f = __builtin_bit_cast(float, u);
+    }
+    return f;
+}
+
+// Turn the pair (a, b) through the angle with cosine c and sine s:
+// (a c - b s, a s + b c).  In fp64 both products of a 16-bit value and an fp32
+// table entry are exact, so each result rounds once (in the difference or sum);
+// the results come back rounded to odd, ready for one nearest-even rounding into
+// the 16-bit storage type.
+__device__ __forceinline__ void rope_rotate(float a, float b, float c, float s, float& ra, float& rb) {
+    const double da = a, db = b, dc = c, ds = s;
+    ra = round_odd_f32(da * dc - db * ds);
+    rb = round_odd_f32(da * ds + db * dc);
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;

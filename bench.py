@@ -167,7 +167,7 @@ def main():
         copy_calibration(args.copy_mib, max(1, args.steps))
         return
 
-    from attention_attn_fwd_02_amd import bwd, fwd, fwd_decode, load_library
+    from attention_attn_fwd_02_amd import bwd, fwd, fwd_decode, fwd_rope, load_library
     from attention_attn_fwd_02_amd import workloads as W
     load_library()
     name = args.workload or W.HEADLINE
@@ -183,7 +183,18 @@ def main():
     stream = torch.cuda.current_stream(dev)
     decode = name in W.DECODE
     backward = name in W.BACKWARD
-    if backward:
+    rope = name in W.ROPE
+    if rope:
+        # rotary embedding on Q and K: the key pass and the attention kernel both
+        # run in every step; tables and the rotated-key buffer are allocated once
+        ct, st = (t.to(dev) for t in W.rope_tables(w.Sk, w.D))
+        k_rot = torch.empty_like(kd)
+        layout = W.ROPE_LAYOUT[name]
+
+        def step():
+            fwd_rope(qd, kd, vd, ct, st, layout=layout, causal=w.causal, scale=w.scale, out=o,
+                     lse=lse, k_rot=k_rot, stream=stream)
+    elif backward:
         # gradients of the forward; its O and LSE are computed once, outside the timing
         from attention_attn_fwd_02_amd import attn_bwd_workspace
         dod = W.make_dout(w, q).to(dev)
@@ -237,13 +248,15 @@ def main():
         return
 
     cpu = None
-    if not args.no_cpu_baseline and not backward:
+    if not args.no_cpu_baseline and not backward and not rope:
         cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
         log("cpu baseline: %.4g TFLOP/s on %d threads" % (cpu["value"], cpu["cores"]))
 
     metric = "attention fwd TFLOP/s (bf16, causal S=4096 D=128) + % of MFMA peak"
     if backward:
         metric = "attention bwd TFLOP/s (bf16, causal S=4096 D=128, 10*D FLOP per pair) + % of MFMA peak"
+    elif rope:
+        metric = "attention fwd with RoPE on Q and K, TFLOP/s (bf16, causal S=4096 D=128) + % of MFMA peak"
     line = {
         "metric": metric,
         "value": round(value, 3),

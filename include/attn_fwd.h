@@ -173,6 +173,45 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              float scale, int causal, int dtype,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Attention with the rotary position embedding applied to Q and K on the way in.
+ *
+ * The FIBER page lists RoPE among the vector operations between the GEMMs of a
+ * transformer block (background; evaluation set-up, "Workloads") and the VDCores
+ * page evaluates QKV projection fused with RoPE (evaluation, dynamic fusion,
+ * Fig. 12).  The rotation is that of the RoPE paper the FIBER page cites: the D
+ * features of a row form D/2 pairs, and pair i of a row at position p becomes
+ *     (a, b) -> (a c - b s, a s + b c),   c = rope_cos[p][i],  s = rope_sin[p][i].
+ * Key j sits at position j; query i at position i + (Sk - Sq) (the alignment of the
+ * causal mask).  Each rotated element is computed in fp64 and rounded once (nearest
+ * even) into `dtype`, so the result equals attn_fwd applied to Q and K first
+ * rotated by a separate step that writes `dtype` tensors.
+ *
+ * attn_fwd_rope -- enqueue two kernels on `stream`: the keys are rotated into
+ * k_rot (one HBM pass), then attn_fwd's kernel runs on k_rot with each query
+ * fragment rotated in registers as it is loaded.
+ *   q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal: as for attn_fwd
+ *   k_rot       [B][Hkv][Sk][D] output, element type `dtype`, 16-byte aligned: the
+ *               rotated keys (what a KV cache holds); must not overlap any input
+ *   rope_cos, rope_sin  [Sk][D/2] fp32 device tables, 16-byte aligned (row p is
+ *               position p; only rows 0 .. Sk-1 are read)
+ *   rope_layout ATTN_ROPE_INTERLEAVED: pairs are features (2i, 2i+1);
+ *               ATTN_ROPE_HALVES: pairs are features (i, i + D/2)
+ * dtype must be ATTN_BF16 or ATTN_FP16 (ATTN_FP32: ATTN_ERR_UNSUPPORTED).  Errors
+ * are those of attn_fwd, plus ATTN_ERR_INVALID_ARG for a null or misaligned k_rot
+ * or table, an unknown layout, or Sq > Sk (queries would sit at negative
+ * positions).  Deterministic; nothing is allocated.
+ */
+typedef enum {
+    ATTN_ROPE_INTERLEAVED = 1,
+    ATTN_ROPE_HALVES = 2
+} attn_rope_layout_t;
+
+int attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse, void* k_rot,
+                  const float* rope_cos, const float* rope_sin, int rope_layout,
+                  int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                  float scale, int causal, int dtype, hipStream_t stream);
+
 /* Static, human-readable name of a return code ("unknown status" otherwise). */
 const char* attn_status_str(int status);
 

@@ -36,7 +36,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"attn_fwd", "attn_status_str", "attn_fwd_decode",
-                          "attn_fwd_decode_workspace", "attn_bwd", "attn_bwd_workspace"}, names
+                          "attn_fwd_decode_workspace", "attn_bwd", "attn_bwd_workspace",
+                          "attn_fwd_rope"}, names
     raw = ctypes.CDLL(A.LIB_PATH)
     for nm in names:
         assert hasattr(raw, nm), nm
@@ -48,6 +49,8 @@ def test_enum_values_match_binding():
     assert _declared_enum("attn_status_t") == {
         "ATTN_OK": A.ATTN_OK, "ATTN_ERR_INVALID_ARG": A.ATTN_ERR_INVALID_ARG,
         "ATTN_ERR_UNSUPPORTED": A.ATTN_ERR_UNSUPPORTED, "ATTN_ERR_LAUNCH": A.ATTN_ERR_LAUNCH}
+    assert _declared_enum("attn_rope_layout_t") == {
+        "ATTN_ROPE_INTERLEAVED": A.ATTN_ROPE_INTERLEAVED, "ATTN_ROPE_HALVES": A.ATTN_ROPE_HALVES}
 
 
 def test_status_strings(lib):
@@ -231,3 +234,44 @@ def test_bwd_invalid_arguments(lib, bad):
                          ids=["fp32", "d96", "d256"])
 def test_bwd_unsupported(lib, bad):
     assert _bcall(**bad) == A.ATTN_ERR_UNSUPPORTED
+
+
+# ---- attention with the rotary embedding (every call below fails validation) ----
+KR_, RC_, RS_ = 0xB0000, 0xC0000, 0xD0000
+RGOOD = dict(q=Q, k=K, v=V, o=O, lse=L, kr=KR_, rc=RC_, rs=RS_, layout=A.ATTN_ROPE_INTERLEAVED,
+             B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=128, scale=0.125, causal=1, dtype=A.ATTN_BF16,
+             stream=None)
+
+
+def _rcall(**kw):
+    a = dict(RGOOD)
+    a.update(kw)
+    return A.attn_fwd_rope(a["q"], a["k"], a["v"], a["o"], a["lse"], a["kr"], a["rc"], a["rs"],
+                           a["layout"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"],
+                           a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+RINVALID = [
+    dict(q=None), dict(k=None), dict(o=None), dict(kr=None), dict(rc=None), dict(rs=None),
+    dict(kr=KR_ + 2), dict(rc=RC_ + 4), dict(rs=RS_ + 8), dict(layout=0), dict(layout=3),
+    dict(Sq=65), dict(Hq=3, Hkv=2), dict(B=0), dict(scale=float("nan")), dict(dtype=9),
+]
+
+
+@pytest.mark.parametrize("bad", RINVALID, ids=[str(b) for b in RINVALID])
+def test_rope_invalid_arguments(lib, bad):
+    assert _rcall(**bad) == A.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(dtype=A.ATTN_FP32), dict(D=96), dict(D=256)],
+                         ids=["fp32", "d96", "d256"])
+def test_rope_unsupported(lib, bad):
+    assert _rcall(**bad) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_rope_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    t = torch.zeros(4, 32)
+    with pytest.raises(ValueError):
+        A.fwd_rope(q, q, q, t, t)
