@@ -117,6 +117,21 @@ __device__ __forceinline__ int tr_lane_base(int lane, int tpitch) {
     return (4 * h + tr_row) * tpitch + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
 }
 
+// Workgroup w -> (group, block).  When the groups split evenly over the 8 XCDs
+// (the dispatcher sends workgroup w to XCD w % 8), all blocks of a group run on one
+// XCD, so the group's streamed operands (Q and dO, or K and V) stay in that XCD's
+// L2.  Blocks of a group are dispatched in order of their index.
+__device__ __forceinline__ void bwd_map(int w, int nblk, int ngrp, int& grp, int& blk) {
+    if (ngrp % 8 == 0) {
+        const int xcd = w & 7, slot = w >> 3;
+        grp = 8 * (slot / nblk) + xcd;
+        blk = slot % nblk;
+    } else {
+        grp = w / nblk;
+        blk = w % nblk;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // D_i = dO_i . O_i and LSE_i * log2(e), one row per D/8 lanes (16 bytes each).
 // ---------------------------------------------------------------------------
@@ -172,8 +187,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int nkb = (p.Sk + 127) / 128;
-    const int kb = blockIdx.x % nkb;
-    const int grp = blockIdx.x / nkb;            // b * Hkv + g
+    int kb, grp;                                 // grp = b * Hkv + g
+    bwd_map(blockIdx.x, nkb, p.B * p.Hkv, grp, kb);
     const int b = grp / p.Hkv, g = grp % p.Hkv;
     const int R = p.Hq / p.Hkv;
     const int off = p.Sk - p.Sq;
@@ -346,11 +361,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int nqb = (p.Sq + 127) / 128;
-    const int qb = blockIdx.x % nqb;
-    const int bh = blockIdx.x / nqb;             // b * Hq + hq
-    const int b = bh / p.Hq, hq = bh % p.Hq;
+    // the query heads of one K/V head form a group, whose blocks are (query block,
+    // head) with the last query blocks (the heaviest under the causal mask) first
     const int R = p.Hq / p.Hkv;
-    const int grp = b * p.Hkv + hq / R;
+    int grp, sb;                                 // grp = b * Hkv + g
+    bwd_map(blockIdx.x, R * nqb, p.B * p.Hkv, grp, sb);
+    const int qb = CAUSAL ? nqb - 1 - sb / R : sb / R;
+    const int b = grp / p.Hkv;
+    const int hq = (grp % p.Hkv) * R + sb % R;
+    const int bh = b * p.Hq + hq;
     const int off = p.Sk - p.Sq;
     const int qw = qb * 128 + 32 * wave;         // first query of this wave
     const int64_t q_row0 = (int64_t)bh * p.Sq;
