@@ -31,7 +31,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-KERNEL_SRC = os.path.join(ROOT, "attention_attn_fwd_02_amd", "csrc", "attn_fwd_kernels.hip")
+CSRC = os.path.join(ROOT, "attention_attn_fwd_02_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "attn_fwd_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # dense MFMA peaks, MI355X
 HBM_PEAK_GBS = 8000.0                                             # HBM3E, MI355X
@@ -41,15 +42,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per launch from profiles/attn_fwd_traffic_<workload>.txt, or None
-    when the summary is absent or was taken on a different kernel source."""
-    path = os.path.join(PROFILES, "attn_fwd_traffic_%s.txt" % workload)
+def committed_traffic(workload: str, prefix: str = "attn_fwd", src: str = KERNEL_SRC):
+    """HBM bytes per launch of the dominant kernel from
+    profiles/<prefix>_traffic_<workload>.txt, or None when the summary is absent or
+    was taken on a different source of that kernel."""
+    path = os.path.join(PROFILES, "%s_traffic_%s.txt" % (prefix, workload))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -57,7 +59,7 @@ def committed_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -139,7 +141,9 @@ def decode_line(args, w, name, wall_ms, kern_ms):
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (kern_ms * 1e-3) / 1e9, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel_ms_per_launch": round(kern_ms, 5)},
+                     "traffic": committed_traffic(name, "attn_decode",
+                                                  os.path.join(CSRC, "attn_decode_kernels.hip")),
+                     "kernel_ms_per_launch": round(kern_ms, 5)},
         "cpu_baseline": None,
     }
 
@@ -275,7 +279,8 @@ def main():
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": committed_traffic(name),
+                     "traffic": (committed_traffic(name, "attn_bwd", os.path.join(CSRC, "attn_bwd_kernels.hip"))
+                                 if backward else committed_traffic(name)),
                      "kernel_ms_per_launch": round(kern_ms, 5)},
         "cpu_baseline": cpu,
     }
