@@ -160,7 +160,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py: the attention library measures one GPU; --gpus %d is not supported "
               "(the attention forward shards over (batch, head) with no exchange, "
               "so N GPUs would each run this one-GPU workload on their share)" % args.gpus,
               file=sys.stderr)
