@@ -261,6 +261,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st)
             s = E::mfma(*(const vec8*)(cur + OFF_QB + b_lane + 32 * st), kf[st], s);
+        // dP = dO V^T, issued before the softmax so that the matrix core works on it
+        // while the weights are computed
+        f32x16 dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+            dp = E::mfma(*(const vec8*)(cur + OFF_OB + b_lane + 32 * st), vf[st], dp);
         // per-register query statistics: query 8(r/4) + 4h + r%4 of the tile
         float l2[16], dd[16];
 #pragma unroll
@@ -289,13 +297,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
             for (int db = 0; db < DBLK; ++db)
                 dvt[db] = E::mfma(tr_frag<vec8, T::TPITCH>(cur + OFF_OT, t_lane, hf, db), bfr, dvt[db]);
         }
-        // dP = dO V^T
-        f32x16 dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st)
-            dp = E::mfma(*(const vec8*)(cur + OFF_OB + b_lane + 32 * st), vf[st], dp);
         // dS = P o (dP - D); dK^T += Q^T dS  (the scale is applied at the end)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
