@@ -34,7 +34,7 @@
 //   * the softmax reference m is raised only when needed (first visible keys, or
 //     a block whose weights sum past 2^8), so the common path has no max pass.
 // fp32 path: the same dataflow with v_mfma_f32_32x32x2_f32 (true fp32 products),
-// 32 queries per wave, 32-key tiles, single-buffered LDS.
+// 32 queries per wave, 32-key tiles in LDS, the next tile prefetched into registers.
 //
 // The mask, the grouped-head mapping and the empty-row convention are those of
 // include/attn_fwd.h.
@@ -561,20 +561,37 @@ __global__ __launch_bounds__(256) void attn_fwd_32(AttnParams p) {
         for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
     float m_run = NEG_INF, l_run = 0.f;
 
+    // K and V tiles go through registers: the next tile's 16-byte loads are issued
+    // before the current tile is computed, so their latency overlaps the MFMAs
+    constexpr int NPF = BN32 * D / 4 / 256;        // float4 per thread per tile and tensor
+    // (rows past Sk, and the tile after the last, are clamped to row 0 and zeroed)
+    float4 kpre[NPF], vpre[NPF];
+#define ATTN32_LOAD_TILE(J)                                                               \
+    _Pragma("unroll") for (int i = 0; i < NPF; ++i) {                                     \
+        const int e = 4 * (tid + 256 * i);                                                \
+        const int row = e / D, col = e % D;                                               \
+        const bool ok = (J) < ntiles && (J) * BN32 + row < p.Sk;                          \
+        const int64_t off32 = ok ? (int64_t)((J) * BN32 + row) * D + col : (int64_t)col;  \
+        const float4 kx = *(const float4*)(Kg + off32);                                   \
+        const float4 vx = *(const float4*)(Vg + off32);                                   \
+        kpre[i] = ok ? kx : make_float4(0.f, 0.f, 0.f, 0.f);                              \
+        vpre[i] = ok ? vx : make_float4(0.f, 0.f, 0.f, 0.f);                              \
+    }
+    ATTN32_LOAD_TILE(0)
     for (int j = 0; j < ntiles; ++j) {
         const int k0 = j * BN32;
         __syncthreads();     // previous tile fully consumed
-        for (int e = tid; e < BN32 * D; e += 256) {
+#pragma unroll
+        for (int i = 0; i < NPF; ++i) {
+            const int e = 4 * (tid + 256 * i);
             const int row = e / D, col = e % D;
-            float kx = 0.f, vx = 0.f;
-            if (k0 + row < p.Sk) {
-                kx = Kg[(int64_t)(k0 + row) * D + col];
-                vx = Vg[(int64_t)(k0 + row) * D + col];
-            }
-            ks[row * KP + col] = kx;
-            vs[row * KP + col] = vx;
+            float* kd = ks + row * KP + col;
+            float* vd = vs + row * KP + col;
+            kd[0] = kpre[i].x; kd[1] = kpre[i].y; kd[2] = kpre[i].z; kd[3] = kpre[i].w;
+            vd[0] = vpre[i].x; vd[1] = vpre[i].y; vd[2] = vpre[i].z; vd[3] = vpre[i].w;
         }
         __syncthreads();
+        ATTN32_LOAD_TILE(j + 1)
         if (k0 >= wkend) continue;
 
         f32x16 sacc;
@@ -641,6 +658,8 @@ __global__ __launch_bounds__(256) void attn_fwd_32(AttnParams p) {
         }
     }
 }
+
+#undef ATTN32_LOAD_TILE
 
 // ---------------------------------------------------------------------------
 // kernel selection
