@@ -47,7 +47,7 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                     i32, vp, sz, vp]
     lib.attn_fwd_decode.restype = i32
-    lib.attn_bwd_workspace.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+    lib.attn_bwd_workspace.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.attn_bwd_workspace.restype = i32
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                              i32, i32, vp, sz, vp]
@@ -80,10 +80,10 @@ def attn_fwd_decode(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype
                                           int(workspace_bytes), stream)
 
 
-def attn_bwd_workspace(B, Hq, Sq):
+def attn_bwd_workspace(B, Hq, Hkv, Sq, Sk, D):
     """(status, bytes) of the C workspace query of the backward."""
     n = ctypes.c_size_t(0)
-    st = load_library().attn_bwd_workspace(B, Hq, Sq, ctypes.byref(n))
+    st = load_library().attn_bwd_workspace(B, Hq, Hkv, Sq, Sk, D, ctypes.byref(n))
     return st, n.value
 
 
@@ -204,7 +204,7 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=No
         raise ValueError("o, lse, dout must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st, need = attn_bwd_workspace(B, Hq, Sq)
+    st, need = attn_bwd_workspace(B, Hq, Hkv, Sq, Sk, D)
     if st != ATTN_OK:
         raise AttnError(st)
     if workspace is None:

@@ -9,9 +9,14 @@
 //     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q
 // Three kernels:
 //   attn_bwd_pre   D_i and LSE_i log2(e) per query row (into the workspace);
-//   attn_bwd_dkdv  one workgroup per (batch, K/V head, 128 keys), 4 waves x 32 keys:
-//                  loops over the query heads of the group and their 32-query tiles,
-//                  accumulating dK^T and dV^T in registers (no atomics);
+//   attn_bwd_dkdv  one workgroup per (batch, K/V head, 128 keys, split), 4 waves x 32
+//                  keys: loops over its share of the query heads of the group and
+//                  their 32-query tiles, accumulating dK^T and dV^T in registers (no
+//                  atomics).  With one split the gradients are stored directly; a
+//                  grouped-query shape with few K/V heads instead splits the query
+//                  heads of a group over several workgroups (fp32 partial sums), so
+//                  the pass fills the GPU, and
+//   attn_bwd_reduce adds the partial sums in split order and stores dK, dV;
 //   attn_bwd_dq    one workgroup per (batch, query head, 128 queries), 4 waves x 32
 //                  queries: loops over 32-key tiles, accumulating dQ^T.
 // Every product is a v_mfma_f32_32x32x16_{bf16,f16} in the layouts of the forward
@@ -98,6 +103,21 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mu
         if (row < nrows)
             *(u32x4*)(out + (row0 + row) * ROW + 16 * (lane % LPR)) = v;
     }
+}
+
+// A wave's 32 x D fp32 result in the same accumulator layout, stored as fp32 rows
+// [0, nrows) of `out` (row pitch D floats): lane n writes 16-byte runs of its row.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(const f32x16 (&acc)[D / 32], float* out, int nrows, int lane) {
+    const int n = lane & 31, h = lane >> 5;
+    if (n >= nrows) return;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 v = {acc[d][4 * g + 0], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
+            *(float4*)(out + n * D + 32 * d + 8 * g + 4 * h) = v;
+        }
 }
 
 // Two transposing reads give lane l the elements X[r0 + j][32 db + l % 32], j = 0..7,
@@ -187,10 +207,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int nkb = (p.Sk + 127) / 128;
-    int kb, grp;                                 // grp = b * Hkv + g
-    bwd_map(blockIdx.x, nkb, p.B * p.Hkv, grp, kb);
+    int kb, sg;                                  // sg = (b * Hkv + g) * nsplit + split
+    bwd_map(blockIdx.x, nkb, p.B * p.Hkv * p.nsplit, sg, kb);
+    const int grp = sg / p.nsplit, split = sg % p.nsplit;
     const int b = grp / p.Hkv, g = grp % p.Hkv;
     const int R = p.Hq / p.Hkv;
+    const int RS = R / p.nsplit;                 // query heads of this split: split*RS ..
     const int off = p.Sk - p.Sq;
     const int k0w = kb * 128 + 32 * wave;        // first key of this wave
     const int64_t kv_row0 = (int64_t)grp * p.Sk;
@@ -208,13 +230,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
         }
     }
 
-    // query tiles: the R heads of the group, each from the first tile whose last
+    // query tiles: the RS heads of the split, each from the first tile whose last
     // query sees this workgroup's first key
     const int nqt = (p.Sq + 31) / 32;
     int qt0 = 0;
     if (CAUSAL) qt0 = max(0, kb * 128 - off) / 32;
     const int per_head = max(0, nqt - qt0);
-    const int ntiles = R * per_head;
+    const int ntiles = RS * per_head;
 
     // DMA: wave 0 stages Q (b128), 1 Q (tr), 2 dO (b128), 3 dO (tr) plus LSE2 and D
     uint32_t vo[BWD_MAXDMA];
@@ -225,7 +247,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
     const uint32_t lvo = lane < 8 ? 16u * lane : OOB_VOFFSET;
     auto dma_tile = [&](int t, uint8_t* dst) {
         const bool live = t < ntiles;
-        const int r = live ? t / per_head : 0;
+        const int r = split * RS + (live ? t / per_head : 0);
         const int q0 = live ? (qt0 + t % per_head) * 32 : 0;
         const int64_t head_row0 = ((int64_t)b * p.Hq + (int64_t)g * R + r) * p.Sq;
         const void* src = (wave < 2) ? p.q : p.dout;
@@ -333,12 +355,45 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
     }
 
     // dK = scale (dK^T)^T, dV = (dV^T)^T, rows k0w .. k0w + 31 below Sk
-    uint8_t* stg = buf1 + wave * (32 * (T::ROW + 16));
-    static_assert(4 * 32 * (T::ROW + 16) <= BUF, "staging fits");
     const int nrows = min(32, p.Sk - k0w);
-    if (nrows > 0) {
+    if (nrows <= 0) return;
+    if (p.nsplit == 1) {
+        uint8_t* stg = buf1 + wave * (32 * (T::ROW + 16));
+        static_assert(4 * 32 * (T::ROW + 16) <= BUF, "staging fits");
         store_rows<DT, D>(dvt, 1.f, stg, (uint8_t*)p.dv, kv_row0 + k0w, nrows, lane);
         store_rows<DT, D>(dkt, p.scale, stg, (uint8_t*)p.dk, kv_row0 + k0w, nrows, lane);
+    } else {
+        // this split's fp32 partial sums (dK unscaled); every row below Sk is written
+        // by every split, zeros where the split's queries see none of the keys
+        float* pk = p.part + (int64_t)(2 * split) * p.kvelems + (kv_row0 + k0w) * D;
+        store_rows_f32<D>(dkt, pk, nrows, lane);
+        store_rows_f32<D>(dvt, pk + p.kvelems, nrows, lane);
+    }
+}
+
+// dK = scale * (sum of the splits' partial dK), dV = sum of the partial dV, the
+// splits added in index order; eight elements of each per thread.
+template <int DT>
+__global__ __launch_bounds__(256) void attn_bwd_reduce(BwdParams p) {
+    typedef Elem16<DT> E;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= p.kvelems) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = 0.f;
+        for (int sp = 0; sp < p.nsplit; ++sp) {
+            const float4* src = (const float4*)(p.part + (int64_t)(2 * sp + t) * p.kvelems + i);
+            const float4 x = src[0], y = src[1];
+            a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w;
+            a[4] += y.x; a[5] += y.y; a[6] += y.z; a[7] += y.w;
+        }
+        const float mul = t == 0 ? p.scale : 1.f;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = E::pack(a[2 * e] * mul, a[2 * e + 1] * mul);
+        *(u32x4*)((uint8_t*)(t == 0 ? p.dk : p.dv) + 2 * i) = w;
     }
 }
 
@@ -488,6 +543,7 @@ template <int DT, int D> static BwdKernels pick_bwd(int causal) {
     k.pre = (const void*)attn_bwd_pre<DT, D>;
     k.dkdv = causal ? (const void*)attn_bwd_dkdv<DT, D, true> : (const void*)attn_bwd_dkdv<DT, D, false>;
     k.dq = causal ? (const void*)attn_bwd_dq<DT, D, true> : (const void*)attn_bwd_dq<DT, D, false>;
+    k.reduce = (const void*)attn_bwd_reduce<DT>;
     return k;
 }
 
@@ -499,7 +555,7 @@ BwdKernels select_bwd(int dtype, int D, int causal) {
         if (D == 64) return pick_bwd<ATTN_IMPL_FP16, 64>(causal);
         if (D == 128) return pick_bwd<ATTN_IMPL_FP16, 128>(causal);
     }
-    BwdKernels none = {nullptr, nullptr, nullptr};
+    BwdKernels none = {nullptr, nullptr, nullptr, nullptr};
     return none;
 }
 

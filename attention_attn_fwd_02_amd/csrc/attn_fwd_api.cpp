@@ -234,10 +234,42 @@ extern "C" int attn_fwd_decode(const void* q, const void* k, const void* v, void
     return ATTN_OK;
 }
 
-extern "C" int attn_bwd_workspace(int B, int Hq, int Sq, size_t* bytes) {
-    if (!bytes || B < 1 || Hq < 1 || Sq < 1) return ATTN_ERR_INVALID_ARG;
-    if (!product_fits(B, Hq, Sq, 8)) return ATTN_ERR_INVALID_ARG;
-    *bytes = (size_t)2 * (size_t)B * (size_t)Hq * (size_t)Sq * sizeof(float);
+namespace {
+
+// Workgroups that share the query heads of one K/V head in the dK/dV pass: doubled
+// (while it divides the Hq/Hkv query heads of a group) until the pass has at least
+// 512 workgroups, two per CU.  One for every shape whose K/V heads already fill it.
+int bwd_splits(int B, int Hq, int Hkv, int Sk) {
+    const int64_t base = (int64_t)B * Hkv * ((Sk + 127) / 128);
+    const int R = Hq / Hkv;
+    int ns = 1;
+    while (base * ns < 512 && R % (2 * ns) == 0) ns *= 2;
+    return ns;
+}
+
+// Bytes of the workspace: two fp32 values per query row, then (several splits) the
+// partial dK and dV of every split, starting on a 256-byte boundary.
+bool bwd_layout(int B, int Hq, int Hkv, int Sq, int Sk, int D, size_t* bytes, size_t* part_off,
+                int* nsplit) {
+    const int ns = bwd_splits(B, Hq, Hkv, Sk);
+    if (!product_fits(B, Hq, Sq, 8) || !product_fits((int64_t)B * Hkv, Sk, D, (int64_t)ns * 8)) return false;
+    const size_t rows_bytes = (size_t)2 * (size_t)B * (size_t)Hq * (size_t)Sq * sizeof(float);
+    const size_t off = (rows_bytes + 255) / 256 * 256;
+    const size_t part = ns > 1 ? (size_t)ns * 2 * (size_t)B * Hkv * Sk * D * sizeof(float) : 0;
+    *bytes = off + part;
+    *part_off = off;
+    *nsplit = ns;
+    return true;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd_workspace(int B, int Hq, int Hkv, int Sq, int Sk, int D, size_t* bytes) {
+    if (!bytes || B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1 || Hq % Hkv != 0)
+        return ATTN_ERR_INVALID_ARG;
+    size_t off;
+    int ns;
+    if (!bwd_layout(B, Hq, Hkv, Sq, Sk, D, bytes, &off, &ns)) return ATTN_ERR_INVALID_ARG;
     return ATTN_OK;
 }
 
@@ -254,15 +286,19 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
         return ATTN_ERR_INVALID_ARG;
     if (dtype == ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)B * Hq * Sq;
-    size_t need = 0;
-    if (attn_bwd_workspace(B, Hq, Sq, &need) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+    size_t need = 0, part_off = 0;
+    int nsplit = 1;
+    if (!bwd_layout(B, Hq, Hkv, Sq, Sk, D, &need, &part_off, &nsplit)) return ATTN_ERR_INVALID_ARG;
     if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
+    const int64_t kvelems = (int64_t)B * Hkv * Sk * D;
     const int64_t n_pre = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
-    const int64_t n_kv = (int64_t)B * Hkv * ((Sk + 127) / 128);
+    const int64_t n_kv = (int64_t)B * Hkv * ((Sk + 127) / 128) * nsplit;
     const int64_t n_q = (int64_t)B * Hq * ((Sq + 127) / 128);
-    if (n_pre > INT32_MAX || n_kv > INT32_MAX || n_q > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    const int64_t n_red = (kvelems / 8 + 255) / 256;
+    if (n_pre > INT32_MAX || n_kv > INT32_MAX || n_q > INT32_MAX || n_red > INT32_MAX)
+        return ATTN_ERR_UNSUPPORTED;
     const BwdKernels kf = select_bwd(dtype, D, causal ? 1 : 0);
-    if (!kf.pre || !kf.dkdv || !kf.dq) return ATTN_ERR_UNSUPPORTED;
+    if (!kf.pre || !kf.dkdv || !kf.dq || !kf.reduce) return ATTN_ERR_UNSUPPORTED;
 
     BwdParams p;
     p.q = q;
@@ -276,6 +312,9 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.dv = dv;
     p.l2row = (float*)workspace;
     p.drow = p.l2row + rows;
+    p.part = nsplit > 1 ? (float*)((uint8_t*)workspace + part_off) : nullptr;
+    p.nsplit = nsplit;
+    p.kvelems = kvelems;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -288,6 +327,9 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (hipLaunchKernel(kf.pre, dim3((unsigned)n_pre), dim3(256), args, 0, stream) != hipSuccess)
         return ATTN_ERR_LAUNCH;
     if (hipLaunchKernel(kf.dkdv, dim3((unsigned)n_kv), dim3(256), args, 0, stream) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    if (nsplit > 1 &&
+        hipLaunchKernel(kf.reduce, dim3((unsigned)n_red), dim3(256), args, 0, stream) != hipSuccess)
         return ATTN_ERR_LAUNCH;
     if (hipLaunchKernel(kf.dq, dim3((unsigned)n_q), dim3(256), args, 0, stream) != hipSuccess)
         return ATTN_ERR_LAUNCH;

@@ -86,12 +86,16 @@ struct BwdParams {
     void* dv;
     float* l2row;       // workspace: LSE * log2(e) per query row
     float* drow;        // workspace: dO . O per query row
+    float* part;        // workspace (nsplit > 1): fp32 partial dK, dV per split,
+                        // [nsplit][2][B*Hkv*Sk*D], dK unscaled
     int B, Hq, Hkv, Sq, Sk;
+    int nsplit;         // workgroups sharing the query heads of one K/V head (divides Hq/Hkv)
     float c;            // scale * log2(e) (any sign)
     float scale;
     int64_t rows;       // B*Hq*Sq
+    int64_t kvelems;    // B*Hkv*Sk*D
 };
-struct BwdKernels { const void* pre; const void* dkdv; const void* dq; };
+struct BwdKernels { const void* pre; const void* dkdv; const void* dq; const void* reduce; };
 BwdKernels select_bwd(int dtype, int D, int causal);   // null members: unsupported
 
 const void* select_decode_split(int dtype, int D, int causal);   // null: unsupported

@@ -141,6 +141,8 @@ BACKWARD = {
     w.name: w for w in [
         Workload("bwd_causal_bf16_b2_h32_s4096_d128", "bf16", 2, 32, 32, 4096, 4096, 128, True,
                  1011, note="backward of the headline forward"),
+        Workload("bwd_gqa8_causal_bf16_b1_hq32_hkv4_s4096_d128", "bf16", 1, 32, 4, 4096, 4096, 128,
+                 True, 1013, note="backward, grouped-query with 8 query heads per K/V head"),
     ]
 }
 

@@ -203,7 +203,7 @@ def main():
         from attention_attn_fwd_02_amd import attn_bwd_workspace
         dod = W.make_dout(w, q).to(dev)
         fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
-        st, nbytes = attn_bwd_workspace(w.B, w.Hq, w.Sq)
+        st, nbytes = attn_bwd_workspace(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
 

@@ -145,11 +145,14 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
  *     dK = scale dS^T Q,
  * with the dK and dV of a key/value head summed over the query heads that read it.
  *
- * attn_bwd_workspace -- device workspace bytes attn_bwd needs (two fp32 values per
- * query row); ATTN_ERR_INVALID_ARG for a null `bytes`, a size < 1 or overflowing
- * sizes.
+ * attn_bwd_workspace -- device workspace bytes attn_bwd needs for these sizes: two
+ * fp32 values per query row and, for grouped-query shapes whose K/V heads alone
+ * give the dK/dV pass fewer than 512 workgroups, fp32 partial dK and dV for each of
+ * the workgroups that share a K/V head's query heads (up to the Hq/Hkv of them);
+ * ATTN_ERR_INVALID_ARG for a null `bytes`, a size < 1, Hq not a multiple of Hkv or
+ * overflowing sizes.
  *
- * attn_bwd -- enqueue the three kernels on `stream`.
+ * attn_bwd -- enqueue the kernels on `stream` (three, four with partial sums).
  *   q, k, v, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype: as given to attn_fwd
  *   o      [B][Hq][Sq][D]  attn_fwd's output for these inputs
  *   lse    [B][Hq][Sq]     attn_fwd's log-sum-exp (fp32, required here)
@@ -166,7 +169,7 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
  * multiply Q, K or dO.  Deterministic: no atomics, fixed summation order.  Keys
  * that no query sees get dK = dV = 0.
  */
-int attn_bwd_workspace(int B, int Hq, int Sq, size_t* bytes);
+int attn_bwd_workspace(int B, int Hq, int Hkv, int Sq, int Sk, int D, size_t* bytes);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv,
              int B, int Hq, int Hkv, int Sq, int Sk, int D,

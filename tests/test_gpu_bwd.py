@@ -3,7 +3,10 @@
 The GPU backward consumes the GPU forward's O and LSE, as a training step would;
 the oracle recomputes everything from the inputs in fp64.  Every element of dQ,
 dK and dV is compared on small and ragged shapes (MHA, GQA, MQA, causal and not,
-Sq != Sk with key-less rows, bf16 and fp16, D = 64 and 128)."""
+Sq != Sk with key-less rows, bf16 and fp16, D = 64 and 128).  The grouped-query
+shapes here have few K/V heads, so the library splits the query heads of each
+K/V head over 2 to 8 workgroups and adds their fp32 partial dK, dV in a separate
+pass; the MHA shapes take the direct path."""
 import zlib
 
 import numpy as np
@@ -70,6 +73,8 @@ SHAPES = [
     ("fp16", 1, 4, 4, 130, 70, 64, False),
     ("bf16", 1, 2, 1, 1, 1, 64, True),
     ("bf16", 1, 2, 2, 1000, 1000, 128, True),    # several key blocks and query tiles
+    ("bf16", 1, 16, 2, 768, 768, 128, True),     # 8 query heads per K/V head over 8 workgroups
+    ("fp16", 1, 8, 1, 300, 260, 64, False),      # MQA, 8 partial sums per key row
 ]
 
 
@@ -133,3 +138,38 @@ def test_bwd_full_size_sampled_heads():
             say("  %s head %s: max|err| %.3g  max|ref| %.3g  tol %.3g"
                 % (name, bh, err, np.abs(want[i]).max(), tol))
             assert err <= tol, "head %s %s: max |err| %.3g > %.3g" % (bh, name, err, tol)
+
+
+def test_bwd_gqa_workload_full_size():
+    """The grouped-query backward workload at full size (B=1, Hq=32, Hkv=4, S=4096,
+    D=128, causal bf16; 8 query heads per K/V head, split over 4 workgroups), in the
+    launch configuration the benchmark times, against the identity that holds at any
+    size: with every K/V head repeated for its query heads the problem becomes MHA,
+    whose dQ is the same and whose dK, dV summed over each group's heads are the
+    grouped dK, dV.  The MHA run takes the direct path (no partial sums); its
+    per-head gradients were checked against the oracle above."""
+    w = W.lookup("bwd_gqa8_causal_bf16_b1_hq32_hkv4_s4096_d128")
+    R = w.Hq // w.Hkv
+    dev = torch.device("cuda:0")
+    q, k, v = W.make_inputs(w)
+    do = W.make_dout(w, q)
+    say("case", w.name)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fwd(qd, kd, vd, causal=True, scale=w.scale)
+    dq, dk, dv = bwd(qd, kd, vd, o, lse, dod, causal=True, scale=w.scale)
+    ke = kd.repeat_interleave(R, dim=1).contiguous()
+    ve = vd.repeat_interleave(R, dim=1).contiguous()
+    o2, lse2 = fwd(qd, ke, ve, causal=True, scale=w.scale)
+    dq2, dk2, dv2 = bwd(qd, ke, ve, o2, lse2, dod, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+    assert torch.equal(dq.view(torch.int16), dq2.view(torch.int16)), "dQ differs from MHA's"
+    for name, got, exp in (("dk", dk, dk2), ("dv", dv, dv2)):
+        want = exp.float().reshape(w.B, w.Hkv, R, w.Sk, w.D).sum(dim=2).double().cpu().numpy()
+        gf = got.cpu().to(torch.float64).numpy()
+        assert not np.isnan(gf).any(), "NaN in " + name
+        err = float(np.abs(gf - want).max())
+        tol = bwd_tolerance(want, w.dtype)
+        say("  %s: max|grouped - summed MHA| %.3g  max|ref| %.3g  tol %.3g"
+            % (name, err, np.abs(want).max(), tol))
+        assert err <= tol, "%s: max |err| %.3g > %.3g" % (name, err, tol)
