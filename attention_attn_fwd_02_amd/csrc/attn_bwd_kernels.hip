@@ -8,9 +8,13 @@
 // forward's LSE and D_i = dO_i . O_i:
 //     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q
 // Three kernels:
-//   attn_bwd_pre   D_i and LSE_i log2(e) per query row (into the workspace);
+//   attn_bwd_pre   -D_i, LSE2_i = LSE_i log2(e) and -LSE2_i / ce per query row (into
+//                  the workspace; ce = scale log2(e), or 2^-100 for a zero scale);
 //   attn_bwd_dkdv  one workgroup per (batch, K/V head, 128 keys, split), 4 waves x 32
-//                  keys: loops over its share of the query heads of the group and
+//                  keys, two workgroups per CU (two waves per SIMD, which is why the
+//                  S and dP accumulators start at -LSE2 / ce and -D instead of holding
+//                  those per-query values in registers of their own): loops over its
+//                  share of the query heads of the group and
 //                  their 32-query tiles, accumulating dK^T and dV^T in registers (no
 //                  atomics).  With one split the gradients are stored directly; a
 //                  grouped-query shape with few K/V heads instead splits the query
@@ -153,7 +157,9 @@ __device__ __forceinline__ void bwd_map(int w, int nblk, int ngrp, int& grp, int
 }
 
 // ---------------------------------------------------------------------------
-// D_i = dO_i . O_i and LSE_i * log2(e), one row per D/8 lanes (16 bytes each).
+// D_i = dO_i . O_i (stored negated), LSE2_i = LSE_i * log2(e) and -LSE2_i / ce, one
+// row per D/8 lanes (16 bytes each).  With ce = 2^-100 (zero scale) the dK/dV pass's
+// S + (-LSE2 / ce) rounds to -LSE2 / ce, whose product with ce is -LSE2 exactly.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre(BwdParams p) {
@@ -181,8 +187,10 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdParams p) {
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
     if (ok && c == 0) {
-        p.drow[row] = acc;
-        p.l2row[row] = p.lse[row] * 1.4426950408889634f;
+        const float l2 = p.lse[row] * 1.4426950408889634f;
+        p.drow[row] = -acc;
+        p.l2row[row] = l2;
+        p.sinit[row] = -l2 / p.ce;
     }
 }
 
@@ -190,13 +198,14 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdParams p) {
 // dK, dV
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv(BwdParams p) {
     typedef Elem16<DT> E;
     typedef typename E::vec8 vec8;
     typedef BwdTile<D> T;
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
-    // one buffer: Q (b128 layout), Q (tr layout), dO (b128), dO (tr), LSE2, D
+    // one buffer: Q (b128 layout), Q (tr layout), dO (b128), dO (tr), -LSE2 / ce, -D
     constexpr int OFF_QB = 0, OFF_QT = T::BREG, OFF_OB = T::BREG + T::TREG;
     constexpr int OFF_OT = 2 * T::BREG + T::TREG, OFF_L = 2 * (T::BREG + T::TREG);
     constexpr int OFF_D = OFF_L + 1024, BUF = OFF_D + 1024;
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
     const int per_head = max(0, nqt - qt0);
     const int ntiles = RS * per_head;
 
-    // DMA: wave 0 stages Q (b128), 1 Q (tr), 2 dO (b128), 3 dO (tr) plus LSE2 and D
+    // DMA: wave 0 stages Q (b128), 1 Q (tr), 2 dO (b128), 3 dO (tr) plus -LSE2 / ce and -D
     uint32_t vo[BWD_MAXDMA];
     const int slots = (wave & 1) ? T::TSLOTS : T::BSLOTS;
     const int ndma = (wave & 1) ? T::TDMA : T::BDMA;
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc((const uint8_t*)src + head_row0 * T::ROW, (uint32_t)p.Sq * T::ROW);
         dma_part(rs, dst + part_off, ndma, vo, live ? (uint32_t)q0 * T::ROW : OOB_VOFFSET);
         if (wave == 3) {
-            const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.l2row + head_row0, (uint32_t)p.Sq * 4);
+            const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.sinit + head_row0, (uint32_t)p.Sq * 4);
             const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.drow + head_row0, (uint32_t)p.Sq * 4);
             const uint32_t so = live ? (uint32_t)q0 * 4 : OOB_VOFFSET;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (lds_void_t*)(dst + OFF_L), 16, lvo, so, 0, 0);
@@ -276,37 +285,36 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
         // nothing to do when every key of the wave is past Sk or past the diagonal
         // of the tile's last query
         if (k0w >= p.Sk || (CAUSAL && k0w > q0 + 31 + off)) return;
-        // S = Q K^T (queries x keys): lane = key column, registers = queries
+        // S = Q K^T - LSE2 / ce (queries x keys): lane = key column, registers =
+        // queries 8(r/4) + 4h + r%4 of the tile; the accumulator starts at the
+        // per-query offset, so that P = exp2(ce S) needs no other per-query value
         f32x16 s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st)
-            s = E::mfma(*(const vec8*)(cur + OFF_QB + b_lane + 32 * st), kf[st], s);
-        // dP = dO V^T, issued before the softmax so that the matrix core works on it
-        // while the weights are computed
-        f32x16 dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st)
-            dp = E::mfma(*(const vec8*)(cur + OFF_OB + b_lane + 32 * st), vf[st], dp);
-        // per-register query statistics: query 8(r/4) + 4h + r%4 of the tile
-        float l2[16], dd[16];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const float4 lv = *(const float4*)(cur + OFF_L + 4 * (8 * gq + 4 * h));
-            const float4 dv4 = *(const float4*)(cur + OFF_D + 4 * (8 * gq + 4 * h));
-            l2[4 * gq + 0] = lv.x; l2[4 * gq + 1] = lv.y; l2[4 * gq + 2] = lv.z; l2[4 * gq + 3] = lv.w;
-            dd[4 * gq + 0] = dv4.x; dd[4 * gq + 1] = dv4.y; dd[4 * gq + 2] = dv4.z; dd[4 * gq + 3] = dv4.w;
+            s[4 * gq + 0] = lv.x; s[4 * gq + 1] = lv.y; s[4 * gq + 2] = lv.z; s[4 * gq + 3] = lv.w;
         }
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+            s = E::mfma(*(const vec8*)(cur + OFF_QB + b_lane + 32 * st), kf[st], s);
+        // dP - D = dO V^T - D, the accumulator starting at -D; issued before the
+        // softmax so that the matrix core works on it while the weights are computed
+        f32x16 dp;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const float4 dv4 = *(const float4*)(cur + OFF_D + 4 * (8 * gq + 4 * h));
+            dp[4 * gq + 0] = dv4.x; dp[4 * gq + 1] = dv4.y; dp[4 * gq + 2] = dv4.z; dp[4 * gq + 3] = dv4.w;
+        }
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+            dp = E::mfma(*(const vec8*)(cur + OFF_OB + b_lane + 32 * st), vf[st], dp);
         const int key = k0w + n;
         float pr[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int qi = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
             const bool vis = !CAUSAL || key <= qi + off;
-            pr[r] = vis ? fast_exp2(fmaf(s[r], p.c, -l2[r])) : 0.f;
+            pr[r] = vis ? fast_exp2(s[r] * p.ce) : 0.f;
         }
         // dV^T += dO^T P
 #pragma unroll
@@ -326,7 +334,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r0 = 8 * hf + 2 * e;
-                bw[e] = E::pack(pr[r0] * (dp[r0] - dd[r0]), pr[r0 + 1] * (dp[r0 + 1] - dd[r0 + 1]));
+                bw[e] = E::pack(pr[r0] * dp[r0], pr[r0 + 1] * dp[r0 + 1]);
             }
             const vec8 bfr = __builtin_bit_cast(vec8, bw);
 #pragma unroll
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
     const int64_t q_row0 = (int64_t)bh * p.Sq;
     const int64_t kv_row0 = (int64_t)grp * p.Sk;
 
-    // this wave's Q and dO rows as MFMA B operands; its query's LSE2 and D
+    // this wave's Q and dO rows as MFMA B operands; its query's LSE2 and -D
     vec8 qf[KSTEPS], of[KSTEPS];
     {
         const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint8_t*)p.q + q_row0 * T::ROW, (uint32_t)p.Sq * T::ROW);
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
     float l2n = 0.f, ddn = 0.f;
     if (qi < p.Sq) {
         l2n = p.l2row[q_row0 + qi];
-        ddn = p.drow[q_row0 + qi];
+        ddn = p.drow[q_row0 + qi];            // -D_i
     }
 
     // key tiles of 32: all of them, or (causal) up to the workgroup's last query's diagonal
@@ -497,7 +505,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
         for (int r = 0; r < 16; ++r) {
             const int key = 8 * (r >> 2) + (r & 3);          // relative to kk0 + 4h
             const float pr = key <= lim ? fast_exp2(fmaf(s[r], p.c, -l2n)) : 0.f;
-            ds[r] = pr * (dp[r] - ddn);
+            ds[r] = pr * (dp[r] + ddn);
         }
         // dQ^T += K^T dS^T
 #pragma unroll

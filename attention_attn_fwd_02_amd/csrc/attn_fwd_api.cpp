@@ -238,22 +238,23 @@ namespace {
 
 // Workgroups that share the query heads of one K/V head in the dK/dV pass: doubled
 // (while it divides the Hq/Hkv query heads of a group) until the pass has at least
-// 512 workgroups, two per CU.  One for every shape whose K/V heads already fill it.
+// 1024 workgroups, two rounds of the two that fit on each CU.  One for every shape
+// whose K/V heads already fill it.
 int bwd_splits(int B, int Hq, int Hkv, int Sk) {
     const int64_t base = (int64_t)B * Hkv * ((Sk + 127) / 128);
     const int R = Hq / Hkv;
     int ns = 1;
-    while (base * ns < 512 && R % (2 * ns) == 0) ns *= 2;
+    while (base * ns < 1024 && R % (2 * ns) == 0) ns *= 2;
     return ns;
 }
 
-// Bytes of the workspace: two fp32 values per query row, then (several splits) the
+// Bytes of the workspace: three fp32 values per query row, then (several splits) the
 // partial dK and dV of every split, starting on a 256-byte boundary.
 bool bwd_layout(int B, int Hq, int Hkv, int Sq, int Sk, int D, size_t* bytes, size_t* part_off,
                 int* nsplit) {
     const int ns = bwd_splits(B, Hq, Hkv, Sk);
-    if (!product_fits(B, Hq, Sq, 8) || !product_fits((int64_t)B * Hkv, Sk, D, (int64_t)ns * 8)) return false;
-    const size_t rows_bytes = (size_t)2 * (size_t)B * (size_t)Hq * (size_t)Sq * sizeof(float);
+    if (!product_fits(B, Hq, Sq, 12) || !product_fits((int64_t)B * Hkv, Sk, D, (int64_t)ns * 8)) return false;
+    const size_t rows_bytes = (size_t)3 * (size_t)B * (size_t)Hq * (size_t)Sq * sizeof(float);
     const size_t off = (rows_bytes + 255) / 256 * 256;
     const size_t part = ns > 1 ? (size_t)ns * 2 * (size_t)B * Hkv * Sk * D * sizeof(float) : 0;
     *bytes = off + part;
@@ -312,6 +313,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.dv = dv;
     p.l2row = (float*)workspace;
     p.drow = p.l2row + rows;
+    p.sinit = p.drow + rows;
     p.part = nsplit > 1 ? (float*)((uint8_t*)workspace + part_off) : nullptr;
     p.nsplit = nsplit;
     p.kvelems = kvelems;
@@ -321,6 +323,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.Sq = Sq;
     p.Sk = Sk;
     p.c = (float)((double)scale * 1.4426950408889634);
+    p.ce = p.c != 0.f ? p.c : 0x1p-100f;
     p.scale = scale;
     p.rows = rows;
     void* args[] = {&p};

@@ -85,12 +85,14 @@ struct BwdParams {
     void* dk;
     void* dv;
     float* l2row;       // workspace: LSE * log2(e) per query row
-    float* drow;        // workspace: dO . O per query row
+    float* drow;        // workspace: -(dO . O) per query row
+    float* sinit;       // workspace: -LSE * log2(e) / ce per query row
     float* part;        // workspace (nsplit > 1): fp32 partial dK, dV per split,
                         // [nsplit][2][B*Hkv*Sk*D], dK unscaled
     int B, Hq, Hkv, Sq, Sk;
     int nsplit;         // workgroups sharing the query heads of one K/V head (divides Hq/Hkv)
     float c;            // scale * log2(e) (any sign)
+    float ce;           // c, or 2^-100 when c is zero (the weights are then exp2(-LSE2))
     float scale;
     int64_t rows;       // B*Hq*Sq
     int64_t kvelems;    // B*Hkv*Sk*D

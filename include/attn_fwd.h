@@ -145,9 +145,9 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
  *     dK = scale dS^T Q,
  * with the dK and dV of a key/value head summed over the query heads that read it.
  *
- * attn_bwd_workspace -- device workspace bytes attn_bwd needs for these sizes: two
+ * attn_bwd_workspace -- device workspace bytes attn_bwd needs for these sizes: three
  * fp32 values per query row and, for grouped-query shapes whose K/V heads alone
- * give the dK/dV pass fewer than 512 workgroups, fp32 partial dK and dV for each of
+ * give the dK/dV pass fewer than 1024 workgroups, fp32 partial dK and dV for each of
  * the workgroups that share a K/V head's query heads (up to the Hq/Hkv of them);
  * ATTN_ERR_INVALID_ARG for a null `bytes`, a size < 1, Hq not a multiple of Hkv or
  * overflowing sizes.

@@ -211,17 +211,17 @@ def _bcall(**kw):
 
 
 def test_bwd_workspace_size(lib):
-    # (B, Hq, Hkv, Sq, Sk, D): two fp32 values per query row; MHA never splits
-    assert A.attn_bwd_workspace(2, 8, 8, 100, 100, 128) == (A.ATTN_OK, 2 * 2 * 8 * 100 * 4)
-    assert A.attn_bwd_workspace(1, 4, 4, 4096, 4096, 64) == (A.ATTN_OK, 2 * 4 * 4096 * 4)
+    # (B, Hq, Hkv, Sq, Sk, D): three fp32 values per query row; MHA never splits
+    assert A.attn_bwd_workspace(2, 8, 8, 100, 100, 128) == (A.ATTN_OK, 3 * 2 * 8 * 100 * 4)
+    assert A.attn_bwd_workspace(1, 4, 4, 4096, 4096, 64) == (A.ATTN_OK, 3 * 4 * 4096 * 4)
     # B=1, 4 K/V heads, 4096 keys: 128 dK/dV workgroups, so the 8 query heads of a
-    # group are split over 4 workgroups (512); each writes fp32 partial dK and dV
-    rows = 2 * 32 * 4096 * 4
+    # group are split over 8 workgroups (1024); each writes fp32 partial dK and dV
+    rows = 3 * 32 * 4096 * 4
     assert A.attn_bwd_workspace(1, 32, 4, 4096, 4096, 128) == (
-        A.ATTN_OK, rows + 4 * 2 * 4 * 4096 * 128 * 4)
+        A.ATTN_OK, rows + 8 * 2 * 4 * 4096 * 128 * 4)
     # the split stops where it no longer divides the group: 2 query heads -> 2 splits;
     # the partial sums start on a 256-byte boundary
-    rows = 2 * 2 * 10 * 4
+    rows = 3 * 2 * 10 * 4
     assert A.attn_bwd_workspace(1, 2, 1, 10, 33, 64) == (
         A.ATTN_OK, (rows + 255) // 256 * 256 + 2 * 2 * 33 * 64 * 4)
     assert A.attn_bwd_workspace(0, 8, 8, 100, 100, 128)[0] == A.ATTN_ERR_INVALID_ARG
@@ -229,7 +229,7 @@ def test_bwd_workspace_size(lib):
     assert A.attn_bwd_workspace(1, 8, 8, 100, 0, 128)[0] == A.ATTN_ERR_INVALID_ARG
     assert A.load_library().attn_bwd_workspace(1, 1, 1, 1, 1, 64, None) == A.ATTN_ERR_INVALID_ARG
     # the size the short-workspace case below is one byte short of
-    assert A.attn_bwd_workspace(1, 4, 2, 64, 64, 128) == (A.ATTN_OK, 2048 + 2 * 2 * 2 * 64 * 128 * 4)
+    assert A.attn_bwd_workspace(1, 4, 2, 64, 64, 128) == (A.ATTN_OK, 3072 + 2 * 2 * 2 * 64 * 128 * 4)
 
 
 BINVALID = [
@@ -237,8 +237,8 @@ BINVALID = [
     dict(dq=None), dict(dk=None), dict(dv=None), dict(do=DO_ + 8), dict(dq=DQ_ + 2),
     dict(dk=DK_ + 4), dict(dv=DV_ + 1), dict(lse=L + 2), dict(Hq=3, Hkv=2), dict(Sk=0),
     dict(scale=float("inf")), dict(dtype=5), dict(ws=None), dict(ws=W_ADDR + 4),
-    dict(ws_bytes=64 * 4 * 8 - 1), 
-    dict(ws_bytes=2048 + 2 * 2 * 2 * 64 * 128 * 4 - 1),   # short by one byte of the partial sums
+    dict(ws_bytes=64 * 4 * 12 - 1), 
+    dict(ws_bytes=3072 + 2 * 2 * 2 * 64 * 128 * 4 - 1),   # short by one byte of the partial sums
 ]
 
 

@@ -88,7 +88,7 @@ def test_bwd_full_output(shape):
     run_bwd(w, seed + 1)
 
 
-@pytest.mark.parametrize("scale", [-0.1, 0.3])
+@pytest.mark.parametrize("scale", [-0.1, 0.0, 0.3])
 def test_bwd_other_scales(scale):
     w = W.custom("bf16", 1, 2, 1, 150, 220, 128, True, seed=8)
     say("case", w.name, "scale", scale)
