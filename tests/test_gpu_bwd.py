@@ -75,6 +75,8 @@ SHAPES = [
     ("bf16", 1, 2, 2, 1000, 1000, 128, True),    # several key blocks and query tiles
     ("bf16", 1, 16, 2, 768, 768, 128, True),     # 8 query heads per K/V head over 8 workgroups
     ("fp16", 1, 8, 1, 300, 260, 64, False),      # MQA, 8 partial sums per key row
+    ("bf16", 1, 6, 2, 300, 300, 128, True),      # three query heads per K/V head: no split
+    ("bf16", 3, 8, 4, 200, 170, 64, True),       # 12 groups, 2 splits each
 ]
 
 

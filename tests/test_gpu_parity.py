@@ -25,6 +25,8 @@ SHAPES = [
     ("bf16", 1, 4, 1, 300, 513, 128, True),      # MQA, fewer queries than keys
     ("bf16", 1, 4, 2, 513, 300, 64, True),       # more queries than keys: empty rows
     ("bf16", 1, 8, 2, 1000, 1000, 128, True),    # GQA, several tiles
+    ("bf16", 1, 6, 2, 300, 300, 128, True),      # three query heads per K/V head
+    ("fp16", 3, 12, 4, 200, 200, 64, False),     # three per K/V head, 12 groups (not a multiple of 8)
     ("bf16", 2, 2, 2, 256, 64, 128, False),
     ("bf16", 1, 2, 2, 64, 700, 64, False),
     ("bf16", 1, 2, 2, 1, 700, 128, True),        # one query against many keys

@@ -48,6 +48,7 @@ SHAPES = [
     ("bf16", 1, 8, 1, 1, 513, 128, True, ATTN_ROPE_INTERLEAVED),
     ("bf16", 1, 2, 2, 1000, 1000, 64, True, ATTN_ROPE_INTERLEAVED),
     ("fp16", 1, 2, 1, 700, 700, 128, True, ATTN_ROPE_HALVES),
+    ("bf16", 1, 6, 2, 300, 300, 128, True, ATTN_ROPE_HALVES),
 ]
 
 
