@@ -3,7 +3,8 @@ bitwise-deterministic results, any stream, no stray writes."""
 import pytest
 import torch
 
-from attention_attn_fwd_02_amd import AttnError, fwd
+from attention_attn_fwd_02_amd import (AttnError, attn_bwd_workspace, attn_fwd_decode_workspace,
+                                       bwd, fwd, fwd_decode, fwd_rope)
 from attention_attn_fwd_02_amd import workloads as W
 from gpu_helpers import run_gpu, say
 
@@ -76,3 +77,74 @@ def test_binding_rejects_bad_shapes_before_launch():
     q3 = torch.zeros(1, 3, 64, 128, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(AttnError):
         fwd(q3, k, v)   # Hq % Hkv != 0
+
+
+PAD = 4096
+
+
+def _window(n, dtype):
+    """A length-n view into a NaN-filled buffer with PAD canary elements on both sides."""
+    big = torch.full((n + 2 * PAD,), float("nan"), dtype=dtype, device=DEV)
+    return big, big[PAD:PAD + n]
+
+
+def _canaries_intact(big, n):
+    return bool(torch.all(torch.isnan(big[:PAD]))) and bool(torch.all(torch.isnan(big[PAD + n:])))
+
+
+def test_bwd_no_writes_outside_outputs_and_workspace():
+    """dQ, dK, dV and the workspace (here with fp32 partial sums: 4 query heads per
+    K/V head split over 4 workgroups) inside canary-filled buffers; only the windows
+    may change, and the gradient windows are fully written."""
+    say("case bwd canaries")
+    B, Hq, Hkv, Sq, Sk, D = 1, 8, 2, 333, 200, 64
+    q, k, v = _inputs("bf16", B, Hq, Hkv, Sq, Sk, D, True, 8)
+    o, lse = fwd(q, k, v, causal=True)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(q.dtype).to(DEV)
+    st, need = attn_bwd_workspace(B, Hq, Hkv, Sq, Sk, D)
+    assert st == 0 and need > 3 * B * Hq * Sq * 4      # the split path is taken
+    bq, dq = _window(q.numel(), q.dtype)
+    bk, dk = _window(k.numel(), k.dtype)
+    bv, dv = _window(v.numel(), v.dtype)
+    bw = torch.full((need + 2 * PAD,), 0xA5, dtype=torch.uint8, device=DEV)
+    ws = bw[PAD:PAD + need]
+    bwd(q, k, v, o, lse, do, causal=True, dq=dq.view(q.shape), dk=dk.view(k.shape),
+        dv=dv.view(v.shape), workspace=ws)
+    torch.cuda.synchronize()
+    for big, win in ((bq, dq), (bk, dk), (bv, dv)):
+        assert _canaries_intact(big, win.numel())
+        assert not torch.any(torch.isnan(win))
+    assert torch.all(bw[:PAD] == 0xA5) and torch.all(bw[PAD + need:] == 0xA5)
+
+
+def test_decode_no_writes_outside_outputs_and_workspace():
+    say("case decode canaries")
+    B, Hq, Hkv, Sq, Sk, D = 3, 8, 2, 1, 1000, 128
+    q, k, v = _inputs("bf16", B, Hq, Hkv, Sq, Sk, D, True, 10)
+    st, need = attn_fwd_decode_workspace(B, Hq, Hkv, Sq, Sk, D, 0)
+    assert st == 0
+    bo, o = _window(q.numel(), q.dtype)
+    bl, lse = _window(B * Hq * Sq, torch.float32)
+    bw = torch.full((need + 2 * PAD,), 0xA5, dtype=torch.uint8, device=DEV)
+    fwd_decode(q, k, v, causal=True, out=o.view(q.shape), lse=lse.view(B, Hq, Sq),
+               workspace=bw[PAD:PAD + need])
+    torch.cuda.synchronize()
+    assert _canaries_intact(bo, o.numel()) and _canaries_intact(bl, lse.numel())
+    assert not torch.any(torch.isnan(o)) and not torch.any(torch.isnan(lse))
+    assert torch.all(bw[:PAD] == 0xA5) and torch.all(bw[PAD + need:] == 0xA5)
+
+
+def test_rope_no_writes_outside_outputs():
+    say("case rope canaries")
+    B, Hq, Hkv, Sq, Sk, D = 1, 4, 2, 300, 300, 128
+    q, k, v = _inputs("bf16", B, Hq, Hkv, Sq, Sk, D, True, 11)
+    ct, stab = (t.to(DEV) for t in W.rope_tables(Sk, D))
+    bo, o = _window(q.numel(), q.dtype)
+    bl, lse = _window(B * Hq * Sq, torch.float32)
+    bk, kr = _window(k.numel(), k.dtype)
+    fwd_rope(q, k, v, ct, stab, causal=True, out=o.view(q.shape), lse=lse.view(B, Hq, Sq),
+             k_rot=kr.view(k.shape))
+    torch.cuda.synchronize()
+    for big, win in ((bo, o), (bl, lse), (bk, kr)):
+        assert _canaries_intact(big, win.numel())
+        assert not torch.any(torch.isnan(win))
