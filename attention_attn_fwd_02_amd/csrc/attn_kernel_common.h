@@ -126,6 +126,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // into a padding slot without touching memory.
 constexpr uint32_t OOB_VOFFSET = 0x7fff0000u;
 
+// cache-policy operand of the buffer intrinsics: the non-temporal hint (nt), for
+// data read exactly once
+constexpr int CPOL_NT = 2;
+
 }  // namespace attn_impl
 
 #endif
