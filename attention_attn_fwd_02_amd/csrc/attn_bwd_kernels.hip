@@ -499,13 +499,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st)
             dp = E::mfma(*(const vec8*)(cur + OFF_VB + b_lane + 32 * st), of[st], dp);
-        const int lim = (CAUSAL ? min(p.Sk - 1, qi + off) : p.Sk - 1) - (kk0 + 4 * h);
+        // the mask only on tiles that cross the diagonal or the end of the keys
         float ds[16];
+        if (kk0 + 32 > p.Sk || (CAUSAL && kk0 + 31 > qw + off)) {
+            const int lim = (CAUSAL ? min(p.Sk - 1, qi + off) : p.Sk - 1) - (kk0 + 4 * h);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r >> 2) + (r & 3);          // relative to kk0 + 4h
-            const float pr = key <= lim ? fast_exp2(fmaf(s[r], p.c, -l2n)) : 0.f;
-            ds[r] = pr * (dp[r] + ddn);
+            for (int r = 0; r < 16; ++r) {
+                const int key = 8 * (r >> 2) + (r & 3);          // relative to kk0 + 4h
+                const float pr = key <= lim ? fast_exp2(fmaf(s[r], p.c, -l2n)) : 0.f;
+                ds[r] = pr * (dp[r] + ddn);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(fmaf(s[r], p.c, -l2n)) * (dp[r] + ddn);
         }
         // dQ^T += K^T dS^T
 #pragma unroll
