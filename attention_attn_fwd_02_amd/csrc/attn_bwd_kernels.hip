@@ -36,6 +36,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_fwd_internal.h"
 #include "attn_kernel_common.h"
 
@@ -246,6 +248,27 @@ void attn_bwd_dkdv(BwdParams p) {
     if (CAUSAL) qt0 = max(0, kb * 128 - off) / 32;
     const int per_head = max(0, nqt - qt0);
     const int ntiles = RS * per_head;
+    // Causal: the first nd query tiles of each head can cross the diagonal of some
+    // wave's keys (the workgroup's last key is kb*128 + 127); they are walked first,
+    // for all heads of the split, with the masked tile code, and the rest without
+    // any per-element compares.  Tile t -> (head, query tile).
+    int nd = 0;
+    if (CAUSAL) {
+        const int x = kb * 128 + 127 - off;
+        nd = x > 0 ? min(per_head, max(0, (x + 31) / 32 - qt0)) : 0;
+    }
+    const int nfull = per_head - nd;
+    const int ndiag = RS * nd;
+    auto tile_at = [&](int t, int& r, int& qt) {
+        if (t < ndiag) {
+            r = t / nd;
+            qt = qt0 + t % nd;
+        } else {
+            const int u = t - ndiag;
+            r = u / nfull;
+            qt = qt0 + nd + u % nfull;
+        }
+    };
 
     // DMA: wave 0 stages Q (b128), 1 Q (tr), 2 dO (b128), 3 dO (tr) plus -LSE2 / ce and -D
     uint32_t vo[BWD_MAXDMA];
@@ -256,8 +279,10 @@ void attn_bwd_dkdv(BwdParams p) {
     const uint32_t lvo = lane < 8 ? 16u * lane : OOB_VOFFSET;
     auto dma_tile = [&](int t, uint8_t* dst) {
         const bool live = t < ntiles;
-        const int r = split * RS + (live ? t / per_head : 0);
-        const int q0 = live ? (qt0 + t % per_head) * 32 : 0;
+        int rr = 0, qt = 0;
+        if (live) tile_at(t, rr, qt);
+        const int r = split * RS + rr;
+        const int q0 = qt * 32;
         const int64_t head_row0 = ((int64_t)b * p.Hq + (int64_t)g * R + r) * p.Sq;
         const void* src = (wave < 2) ? p.q : p.dout;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc((const uint8_t*)src + head_row0 * T::ROW, (uint32_t)p.Sq * T::ROW);
@@ -280,8 +305,14 @@ void attn_bwd_dkdv(BwdParams p) {
     const int b_lane = n * T::BPITCH + 16 * h;
     const int t_lane = tr_lane_base(lane, T::TPITCH);
 
-    auto tile = [&](int t, const uint8_t* cur) {
-        const int q0 = (qt0 + t % per_head) * 32;
+    // one query tile; `masked`: the causal mask is applied (the tiles that may cross
+    // a wave's diagonal; keys past Sk need none: their K, V rows read as zero and
+    // their dK, dV rows are not stored)
+    auto tile = [&](int t, const uint8_t* cur, auto masked) __attribute__((always_inline)) {
+        constexpr bool MASKED = CAUSAL && decltype(masked)::value;
+        int rr, qt;
+        tile_at(t, rr, qt);
+        const int q0 = qt * 32;
         // nothing to do when every key of the wave is past Sk or past the diagonal
         // of the tile's last query
         if (k0w >= p.Sk || (CAUSAL && k0w > q0 + 31 + off)) return;
@@ -313,7 +344,7 @@ void attn_bwd_dkdv(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int qi = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool vis = !CAUSAL || key <= qi + off;
+            const bool vis = !MASKED || key <= qi + off;
             pr[r] = vis ? fast_exp2(s[r] * p.ce) : 0.f;
         }
         // dV^T += dO^T P
@@ -346,19 +377,34 @@ void attn_bwd_dkdv(BwdParams p) {
     dma_tile(0, buf0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
+    // masked pairs of tiles up to an even count covering the diagonal ones, then
+    // unmasked pairs; an odd last tile takes the masked code (right for any tile)
+    const std::true_type MASK;
+    const std::false_type NOMASK;
+    const int nmask = min((ndiag + 1) & ~1, ntiles & ~1);
     int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
+    for (; t < nmask; t += 2) {
         dma_tile(t + 1, buf1);
-        tile(t, buf0);
+        tile(t, buf0, MASK);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         dma_tile(t + 2, buf0);
-        tile(t + 1, buf1);
+        tile(t + 1, buf1, MASK);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    }
+    for (; t + 1 < ntiles; t += 2) {
+        dma_tile(t + 1, buf1);
+        tile(t, buf0, NOMASK);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        dma_tile(t + 2, buf0);
+        tile(t + 1, buf1, NOMASK);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
     if (t < ntiles) {
-        tile(t, buf0);
+        tile(t, buf0, MASK);
         __syncthreads();
     }
 
