@@ -7,29 +7,31 @@
 // score recomputation).  With P_ij = exp(scale q_i.k_j - LSE_i) recomputed from the
 // forward's LSE and D_i = dO_i . O_i:
 //     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q
-// Three kernels:
+// Kernels (in stream order):
 //   attn_bwd_pre   -D_i, LSE2_i = LSE_i log2(e) and -LSE2_i / ce per query row (into
 //                  the workspace; ce = scale log2(e), or 2^-100 for a zero scale);
-//   attn_bwd_dkdv  one workgroup per (batch, K/V head, 128 keys, split), 4 waves x 32
+//   attn_bwd_main  the two passes below in one launch (the dQ workgroups fill the CUs
+//                  the dK/dV pass's last workgroups leave idle):
+//     dK/dV pass   one workgroup per (batch, K/V head, 128 keys, split), 4 waves x 32
 //                  keys, two workgroups per CU (two waves per SIMD, which is why the
 //                  S and dP accumulators start at -LSE2 / ce and -D instead of holding
 //                  those per-query values in registers of their own): loops over its
-//                  share of the query heads of the group and
-//                  their 32-query tiles, accumulating dK^T and dV^T in registers (no
-//                  atomics).  With one split the gradients are stored directly; a
-//                  grouped-query shape with few K/V heads instead splits the query
-//                  heads of a group over several workgroups (fp32 partial sums), so
-//                  the pass fills the GPU, and
-//   attn_bwd_reduce adds the partial sums in split order and stores dK, dV;
-//   attn_bwd_dq    one workgroup per (batch, query head, 128 queries), 4 waves x 32
-//                  queries: loops over 32-key tiles, accumulating dQ^T.
+//                  share of the query heads of the group and their 32-query tiles,
+//                  accumulating dK^T and dV^T in registers (no atomics).  With one
+//                  split the gradients are stored directly; a grouped-query shape with
+//                  few K/V heads instead splits the query heads of a group over
+//                  several workgroups (fp32 partial sums), so the pass fills the GPU;
+//     dQ pass      one workgroup per (batch, query head, 128 queries), 4 waves x 32
+//                  queries: loops over 32-key tiles, accumulating dQ^T;
+//   attn_bwd_reduce (split shapes only) adds the partial sums in split order and
+//                  stores dK, dV.
 // Every product is a v_mfma_f32_32x32x16_{bf16,f16} in the layouts of the forward
 // kernel: an operand whose contraction index runs along memory rows (Q, dO, K, V
 // read as "rows x d") comes from LDS by ds_read_b128 out of rows padded by 16 bytes;
 // one whose contraction index runs down a column (dO^T, Q^T, K^T) comes by
 // ds_read_b64_tr_b16 out of rows padded by 64 bytes; the weights P and dS go from
 // the accumulator registers straight into the next MFMA as packed 16-bit operands.
-// Q, dO (dK/dV kernel) and K (dQ kernel) are therefore staged in both layouts.
+// Q, dO (dK/dV pass) and K (dQ pass) are therefore staged in both layouts.
 // dQ is computed by its own pass rather than by atomic adds so that every gradient
 // is deterministic.
 #include <hip/hip_runtime.h>
@@ -199,9 +201,14 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
+template <int DT, int D> struct DkdvLds {
+    typedef BwdTile<D> T;
+    // one buffer: Q (b128 layout), Q (tr layout), dO (b128), dO (tr), -LSE2 / ce, -D
+    static constexpr int BUF = 2 * (T::BREG + T::TREG) + 2048;
+};
+
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bwd_dkdv(BwdParams p) {
+__device__ __forceinline__ void dkdv_body(const BwdParams& p, const int wid, uint8_t* buf0, uint8_t* buf1) {
     typedef Elem16<DT> E;
     typedef typename E::vec8 vec8;
     typedef BwdTile<D> T;
@@ -211,15 +218,14 @@ void attn_bwd_dkdv(BwdParams p) {
     constexpr int OFF_QB = 0, OFF_QT = T::BREG, OFF_OB = T::BREG + T::TREG;
     constexpr int OFF_OT = 2 * T::BREG + T::TREG, OFF_L = 2 * (T::BREG + T::TREG);
     constexpr int OFF_D = OFF_L + 1024, BUF = OFF_D + 1024;
-    __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
-    __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
+    static_assert(BUF == DkdvLds<DT, D>::BUF, "dK/dV buffer layout");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int nkb = (p.Sk + 127) / 128;
     int kb, sg;                                  // sg = (b * Hkv + g) * nsplit + split
-    bwd_map(blockIdx.x, nkb, p.B * p.Hkv * p.nsplit, sg, kb);
+    bwd_map(wid, nkb, p.B * p.Hkv * p.nsplit, sg, kb);
     const int grp = sg / p.nsplit, split = sg % p.nsplit;
     const int b = grp / p.Hkv, g = grp % p.Hkv;
     const int R = p.Hq / p.Hkv;
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce(BwdParams p) {
 // dQ
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
+__device__ __forceinline__ void dq_body(const BwdParams& p, const int wid, uint8_t* buf0, uint8_t* buf1, const int buf_bytes) {
     typedef Elem16<DT> E;
     typedef typename E::vec8 vec8;
     typedef BwdTile<D> T;
@@ -464,8 +470,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
     // one buffer: K (b128 layout), K (tr layout), V (b128 layout)
     constexpr int OFF_KB = 0, OFF_KT = T::BREG, OFF_VB = T::BREG + T::TREG;
     constexpr int BUF = 2 * T::BREG + T::TREG;
-    __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
-    __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
+    (void)buf_bytes;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -475,7 +480,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
     // head) with the last query blocks (the heaviest under the causal mask) first
     const int R = p.Hq / p.Hkv;
     int grp, sb;                                 // grp = b * Hkv + g
-    bwd_map(blockIdx.x, R * nqb, p.B * p.Hkv, grp, sb);
+    bwd_map(wid, R * nqb, p.B * p.Hkv, grp, sb);
     const int qb = CAUSAL ? nqb - 1 - sb / R : sb / R;
     const int b = grp / p.Hkv;
     const int hq = (grp % p.Hkv) * R + sb % R;
@@ -598,11 +603,29 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(BwdParams p) {
     if (nrows > 0) store_rows<DT, D>(dqt, p.scale, stg, (uint8_t*)p.dq, q_row0 + qw, nrows, lane);
 }
 
+// ---------------------------------------------------------------------------
+// The dK/dV and dQ passes in one launch: workgroups [0, n_kv) run the dK/dV pass,
+// [q_start, q_start + the dQ count) the dQ pass (q_start = n_kv rounded up to a
+// multiple of 8, so that both keep their XCD mapping; the workgroups between exit).
+// The dispatcher hands out workgroups in order, so dQ workgroups fill the CUs that
+// the last dK/dV workgroups leave idle.  Both passes share the two LDS buffers.
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_main(BwdParams p) {
+    constexpr int BUF = DkdvLds<DT, D>::BUF;
+    static_assert(2 * BwdTile<D>::BREG + BwdTile<D>::TREG <= BUF, "dQ buffers fit");
+    __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
+    const int w = blockIdx.x;
+    if (w < p.n_kv) dkdv_body<DT, D, CAUSAL>(p, w, buf0, buf1);
+    else if (w >= p.q_start) dq_body<DT, D, CAUSAL>(p, w - p.q_start, buf0, buf1, BUF);
+}
+
 template <int DT, int D> static BwdKernels pick_bwd(int causal) {
     BwdKernels k;
     k.pre = (const void*)attn_bwd_pre<DT, D>;
-    k.dkdv = causal ? (const void*)attn_bwd_dkdv<DT, D, true> : (const void*)attn_bwd_dkdv<DT, D, false>;
-    k.dq = causal ? (const void*)attn_bwd_dq<DT, D, true> : (const void*)attn_bwd_dq<DT, D, false>;
+    k.main = causal ? (const void*)attn_bwd_main<DT, D, true> : (const void*)attn_bwd_main<DT, D, false>;
     k.reduce = (const void*)attn_bwd_reduce<DT>;
     return k;
 }
@@ -615,7 +638,7 @@ BwdKernels select_bwd(int dtype, int D, int causal) {
         if (D == 64) return pick_bwd<ATTN_IMPL_FP16, 64>(causal);
         if (D == 128) return pick_bwd<ATTN_IMPL_FP16, 128>(causal);
     }
-    BwdKernels none = {nullptr, nullptr, nullptr, nullptr};
+    BwdKernels none = {nullptr, nullptr, nullptr};
     return none;
 }
 

@@ -296,10 +296,11 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     const int64_t n_kv = (int64_t)B * Hkv * ((Sk + 127) / 128) * nsplit;
     const int64_t n_q = (int64_t)B * Hq * ((Sq + 127) / 128);
     const int64_t n_red = (kvelems / 8 + 255) / 256;
-    if (n_pre > INT32_MAX || n_kv > INT32_MAX || n_q > INT32_MAX || n_red > INT32_MAX)
+    const int64_t q_start = (n_kv + 7) / 8 * 8;
+    if (n_pre > INT32_MAX || q_start + n_q > INT32_MAX || n_red > INT32_MAX)
         return ATTN_ERR_UNSUPPORTED;
     const BwdKernels kf = select_bwd(dtype, D, causal ? 1 : 0);
-    if (!kf.pre || !kf.dkdv || !kf.dq || !kf.reduce) return ATTN_ERR_UNSUPPORTED;
+    if (!kf.pre || !kf.main || !kf.reduce) return ATTN_ERR_UNSUPPORTED;
 
     BwdParams p;
     p.q = q;
@@ -317,6 +318,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.part = nsplit > 1 ? (float*)((uint8_t*)workspace + part_off) : nullptr;
     p.nsplit = nsplit;
     p.kvelems = kvelems;
+    p.n_kv = (int)n_kv;
+    p.q_start = (int)q_start;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -329,12 +332,10 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     void* args[] = {&p};
     if (hipLaunchKernel(kf.pre, dim3((unsigned)n_pre), dim3(256), args, 0, stream) != hipSuccess)
         return ATTN_ERR_LAUNCH;
-    if (hipLaunchKernel(kf.dkdv, dim3((unsigned)n_kv), dim3(256), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(kf.main, dim3((unsigned)(q_start + n_q)), dim3(256), args, 0, stream) != hipSuccess)
         return ATTN_ERR_LAUNCH;
     if (nsplit > 1 &&
         hipLaunchKernel(kf.reduce, dim3((unsigned)n_red), dim3(256), args, 0, stream) != hipSuccess)
-        return ATTN_ERR_LAUNCH;
-    if (hipLaunchKernel(kf.dq, dim3((unsigned)n_q), dim3(256), args, 0, stream) != hipSuccess)
         return ATTN_ERR_LAUNCH;
     return ATTN_OK;
 }

@@ -96,8 +96,10 @@ struct BwdParams {
     float scale;
     int64_t rows;       // B*Hq*Sq
     int64_t kvelems;    // B*Hkv*Sk*D
+    int n_kv;           // dK/dV workgroups of the combined launch
+    int q_start;        // first dQ workgroup (n_kv rounded up to a multiple of 8)
 };
-struct BwdKernels { const void* pre; const void* dkdv; const void* dq; const void* reduce; };
+struct BwdKernels { const void* pre; const void* main; const void* reduce; };
 BwdKernels select_bwd(int dtype, int D, int causal);   // null members: unsupported
 
 const void* select_decode_split(int dtype, int D, int causal);   // null: unsupported

@@ -152,7 +152,7 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
  * ATTN_ERR_INVALID_ARG for a null `bytes`, a size < 1, Hq not a multiple of Hkv or
  * overflowing sizes.
  *
- * attn_bwd -- enqueue the kernels on `stream` (three, four with partial sums).
+ * attn_bwd -- enqueue the kernels on `stream` (two, three with partial sums).
  *   q, k, v, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype: as given to attn_fwd
  *   o      [B][Hq][Sq][D]  attn_fwd's output for these inputs
  *   lse    [B][Hq][Sq]     attn_fwd's log-sum-exp (fp32, required here)
