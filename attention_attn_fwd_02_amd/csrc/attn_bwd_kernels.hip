@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce(BwdParams p) {
 // dQ
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool CAUSAL>
-__device__ __forceinline__ void dq_body(const BwdParams& p, const int wid, uint8_t* buf0, uint8_t* buf1, const int buf_bytes) {
+__device__ __forceinline__ void dq_body(const BwdParams& p, const int wid, uint8_t* buf0, uint8_t* buf1) {
     typedef Elem16<DT> E;
     typedef typename E::vec8 vec8;
     typedef BwdTile<D> T;
@@ -470,7 +470,6 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const int wid, uint8
     // one buffer: K (b128 layout), K (tr layout), V (b128 layout)
     constexpr int OFF_KB = 0, OFF_KT = T::BREG, OFF_VB = T::BREG + T::TREG;
     constexpr int BUF = 2 * T::BREG + T::TREG;
-    (void)buf_bytes;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -619,7 +618,7 @@ void attn_bwd_main(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
     const int w = blockIdx.x;
     if (w < p.n_kv) dkdv_body<DT, D, CAUSAL>(p, w, buf0, buf1);
-    else if (w >= p.q_start) dq_body<DT, D, CAUSAL>(p, w - p.q_start, buf0, buf1, BUF);
+    else if (w >= p.q_start) dq_body<DT, D, CAUSAL>(p, w - p.q_start, buf0, buf1);
 }
 
 template <int DT, int D> static BwdKernels pick_bwd(int causal) {
