@@ -97,7 +97,7 @@ constexpr float RESCALE_SUM = 256.0f;      // 2^RESCALE_LOG2
 // after every MFMA (the rest of the softmax fills in behind them) and the LDS
 // reads kept PHASE_LOOKAHEAD MFMAs ahead of their use.
 constexpr int PHASE_VALU = 2;
-constexpr int PHASE_LOOKAHEAD = 2;
+constexpr int PHASE_LOOKAHEAD = 4;
 // LDS reads that must have been issued before MFMA i of the phase
 template <int KS, int DB> constexpr int phase_reads(int i) {
     return i >= KS + 2 * DB ? KS + 4 * DB : (i < KS ? i + 1 : KS + 2 * (i - KS + 1));
