@@ -17,6 +17,12 @@ The line carries:
   cpu_baseline          the fp64 CPU oracle timed on a bounded sample of the same
                         workload on this host (a reported baseline, not a target)
 
+`--workload NAME` selects any workload of attention_attn_fwd_02_amd/workloads.py: the
+forward configurations and variants, split-KV decoding (GB/s against the HBM peak),
+the backward (dQ, dK, dV from the forward's O and LSE; 10*D FLOPs per visible pair)
+and attention with the rotary embedding.  The library measures one GPU: `--gpus N`
+with N > 1 exits with a message.
+
 `--copy-mib N` instead runs N-MiB device copies (the calibration kernel for the
 FETCH_SIZE / WRITE_SIZE counters).
 """
