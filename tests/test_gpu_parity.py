@@ -105,3 +105,30 @@ def test_full_size_sampled(name):
     vmax = v.to(torch.float32).amax().item()
     of = o.to(torch.float32)
     assert of.amin().item() >= vmin - TOL_O[w.dtype] and of.amax().item() <= vmax + TOL_O[w.dtype]
+
+
+def test_long_context_large_offsets():
+    """About a million keys per K/V head (K and V 256 MiB each, byte offsets near
+    2^28 inside a head, 15,626 key tiles per workgroup and a ragged last one): the
+    prefill kernel on sampled rows, and split-KV decoding of the last query row,
+    against the oracle."""
+    from attention_attn_fwd_02_amd import fwd, fwd_decode
+    w = W.custom("bf16", 1, 2, 1, 256, 1_000_003, 128, True, seed=4242)
+    say("case", w.name)
+    q, k, v = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o, lse = fwd(qd, kd, vd, causal=True)
+    o1, l1 = fwd_decode(qd[:, :, -1:].contiguous(), kd, vd, causal=True)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, 63, 64, 127, 128, 255, 256, 300, 511}
+                           | set(np.random.default_rng(5).integers(0, 512, 22).tolist())))
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=True, rows=rows)
+    og = o.reshape(-1, w.D)[torch.from_numpy(rows)].cpu()
+    lg = lse.reshape(-1)[torch.from_numpy(rows)].cpu()
+    e = compare(og, lg, o_ref, lse_ref, "bf16", w.name)
+    say("  prefill, %d rows: max|dO| %.3g  max|dLSE| %.3g" % ((len(rows),) + e))
+    last = np.array([255, 511])            # the last query of each head
+    o_ref1, lse_ref1 = oracle.attn_fwd(q, k, v, causal=True, rows=last)
+    e1 = compare(o1.reshape(-1, w.D).cpu(), l1.reshape(-1).cpu(), o_ref1, lse_ref1, "bf16", w.name)
+    say("  decode, last rows: max|dO| %.3g  max|dLSE| %.3g" % e1)
