@@ -607,10 +607,12 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const int wid, uint8
 // [q_start, q_start + the dQ count) the dQ pass (q_start = n_kv rounded up to a
 // multiple of 8, so that both keep their XCD mapping; the workgroups between exit).
 // The dispatcher hands out workgroups in order, so dQ workgroups fill the CUs that
-// the last dK/dV workgroups leave idle.  Both passes share the two LDS buffers.
+// the last dK/dV workgroups leave idle.  Both passes share the two LDS buffers.  At
+// D = 64 the buffers take 48 KiB and the passes fit 168 registers: three workgroups
+// (three waves per SIMD) per CU; at D = 128, 80 KiB and 256 registers: two.
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 void attn_bwd_main(BwdParams p) {
     constexpr int BUF = DkdvLds<DT, D>::BUF;
     static_assert(2 * BwdTile<D>::BREG + BwdTile<D>::TREG <= BUF, "dQ buffers fit");
