@@ -1,7 +1,7 @@
 /*
  * attn_oracle.c -- plain fp64 CPU oracle for the fused attention forward.
  *
- * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only the
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle, not the product: only the
  * test-suite, the smoke check and the CPU-baseline leg of the benchmark load the
  * library built from it.  It shares no code, header, table or helper with the
  * HIP path, and the HIP path never calls it.

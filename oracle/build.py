@@ -1,6 +1,6 @@
 """Build the fp64 CPU oracle (test infrastructure only) with gcc.
 
-The oracle is the checker for the HIP attention path; building it is part of
+The oracle is the reference the HIP attention path is tested against; building it is part of
 the project's build step, but only the tests, the smoke check and the
 benchmark's CPU-baseline leg ever load it.
 """
