@@ -25,6 +25,13 @@
  * nearest even) before they multiply V, and O is rounded once to the input type.
  * fp32 inputs use fp32 products throughout.  Non-finite inputs propagate; they
  * are not checked.
+ *
+ * Execution: every entry point validates its arguments on the host, then only
+ * enqueues kernel launches on the given stream: it allocates no memory, issues
+ * no memset or copy and does not synchronise.  Calls may therefore be captured
+ * into a HIP graph (stream capture) and replayed; a replay reads the buffers'
+ * contents at replay time.  Every kernel reduces in a fixed order without
+ * atomics, so equal inputs give bit-identical outputs from run to run.
  */
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
