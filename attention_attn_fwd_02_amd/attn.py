@@ -126,8 +126,11 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True, st
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer(out, "out", q.shape, q.dtype, q.device)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _check_buffer(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -142,6 +145,8 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True, st
 def _check_inputs(q, k, v):
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
@@ -152,6 +157,23 @@ def _check_inputs(q, k, v):
         raise ValueError("shape mismatch: q%s k%s v%s" % (tuple(q.shape), tuple(k.shape),
                                                           tuple(v.shape)))
     return B, Hq, Hkv, Sq, Sk, D
+
+
+def _check_buffer(t, name, shape, dtype, device):
+    """A caller-supplied output: on q's device, contiguous, of the exact shape and
+    dtype the kernels write (they write every element of it and nothing past it)."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must be a device tensor on %s" % (name, device))
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError("%s must be %s %s, got %s %s" % (name, list(shape), dtype,
+                                                           list(t.shape), t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_workspace(t, device):
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor on %s" % device)
 
 
 def fwd_decode(q, k, v, causal=False, scale=None, nsplit=0, out=None, lse=None, want_lse=True,
@@ -171,10 +193,14 @@ def fwd_decode(q, k, v, causal=False, scale=None, nsplit=0, out=None, lse=None, 
         raise AttnError(st)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer(out, "out", q.shape, q.dtype, q.device)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _check_buffer(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -209,9 +235,16 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=No
         raise AttnError(st)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for t, name, like in ((o, "o", q), (dout, "dout", q), (lse, "lse", None), (dq, "dq", q),
+                          (dk, "dk", k), (dv, "dv", v)):
+        if like is None:
+            _check_buffer(t, name, (B, Hq, Sq), torch.float32, q.device)
+        else:
+            _check_buffer(t, name, like.shape, like.dtype, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -235,18 +268,22 @@ def fwd_rope(q, k, v, rope_cos, rope_sin, layout=ATTN_ROPE_INTERLEAVED, causal=F
     import torch
     B, Hq, Hkv, Sq, Sk, D = _check_inputs(q, k, v)
     for t in (rope_cos, rope_sin):
-        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("rope tables must be contiguous fp32 device tensors")
+        if not t.is_cuda or t.device != q.device or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("rope tables must be contiguous fp32 tensors on q's device")
         if t.dim() != 2 or t.shape[1] != D // 2 or t.shape[0] < Sk:
             raise ValueError("rope tables must be [P >= Sk, D/2]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer(out, "out", q.shape, q.dtype, q.device)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _check_buffer(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
     if k_rot is None:
         k_rot = torch.empty_like(k)
+    _check_buffer(k_rot, "k_rot", k.shape, k.dtype, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = attn_fwd_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

@@ -79,6 +79,42 @@ def test_binding_rejects_bad_shapes_before_launch():
         fwd(q3, k, v)   # Hq % Hkv != 0
 
 
+def test_binding_rejects_bad_output_buffers_before_launch():
+    """Caller-supplied outputs and workspaces of the wrong shape, dtype, layout or
+    device raise before anything is launched (a short buffer would otherwise be
+    written past its end)."""
+    q, k, v = _inputs("bf16", 1, 4, 2, 64, 64, 128, True, 8)
+    B, Hq, Sq = 1, 4, 64
+    lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=DEV)
+    bad_out = [torch.empty(1, 4, 63, 128, dtype=torch.bfloat16, device=DEV),       # short
+               torch.empty(1, 4, 64, 128, dtype=torch.float16, device=DEV),       # dtype
+               torch.empty(1, 4, 128, 64, dtype=torch.bfloat16, device=DEV).transpose(2, 3),
+               torch.empty(1, 4, 64, 128, dtype=torch.bfloat16)]                  # host
+    for o in bad_out:
+        with pytest.raises(ValueError):
+            fwd(q, k, v, causal=True, out=o)
+        with pytest.raises(ValueError):
+            fwd_rope(q, k, v, *(t.to(DEV) for t in W.rope_tables(64, 128)), causal=True, out=o)
+    for l in (torch.empty(B, Hq, Sq - 1, dtype=torch.float32, device=DEV),
+              torch.empty(B, Hq, Sq, dtype=torch.bfloat16, device=DEV)):
+        with pytest.raises(ValueError):
+            fwd(q, k, v, causal=True, lse=l)
+    o, lse = fwd(q, k, v, causal=True)
+    dout = torch.zeros_like(q)
+    for kw in ({"dq": torch.empty_like(k)}, {"dk": torch.empty_like(q)},
+               {"dv": torch.empty(1, 2, 64, 128, dtype=torch.float32, device=DEV)},
+               {"workspace": torch.empty(64, dtype=torch.uint8)}):
+        with pytest.raises(ValueError):
+            bwd(q, k, v, o, lse, dout, causal=True, **kw)
+    with pytest.raises(ValueError):
+        fwd_rope(q, k, v, *(t.to(DEV) for t in W.rope_tables(64, 128)), causal=True,
+                 k_rot=torch.empty_like(q))
+    qd = q[:, :, :1].contiguous()
+    with pytest.raises(ValueError):
+        fwd_decode(qd, k, v, out=torch.empty_like(q))
+    torch.cuda.synchronize()
+
+
 PAD = 4096
 
 
