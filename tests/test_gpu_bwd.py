@@ -90,8 +90,10 @@ def test_bwd_full_output(shape):
     run_bwd(w, seed + 1)
 
 
-@pytest.mark.parametrize("scale", [-0.1, 0.0, 0.3])
+@pytest.mark.parametrize("scale", [-0.125, -0.1, 0.0, 0.125, 0.3, 1e-39, -2e-38])
 def test_bwd_other_scales(scale):
+    """Signs, zero, and scales so small (a subnormal one included) that the scores
+    contribute nothing: the weights are then 1/|J_i| of each row."""
     w = W.custom("bf16", 1, 2, 1, 150, 220, 128, True, seed=8)
     say("case", w.name, "scale", scale)
     run_bwd(w, 9, scale=scale)
@@ -127,19 +129,24 @@ def test_bwd_full_size_sampled_heads():
     torch.cuda.synchronize()
     for t in (dq, dk, dv):
         assert not torch.isnan(t).any(), "NaN in a gradient (unwritten or invalid)"
-    heads = ((0, 0), (1, 31), (0, 17))
+    # sixteen whole heads of both batches (a quarter of the problem): the first and
+    # last heads and fourteen drawn with a fixed seed
+    rng = np.random.default_rng(w.seed)
+    drawn = [divmod(int(x), w.Hq) for x in rng.choice(np.arange(1, w.B * w.Hq - 1), 14, replace=False)]
+    heads = tuple([(0, 0), (w.B - 1, w.Hq - 1)] + drawn)
     say("case", w.name, "heads", heads)
     # the chosen heads stacked as a batch of one-head problems (one oracle thread each)
     sl = lambda t: torch.cat([t[b:b + 1, h:h + 1] for b, h in heads]).contiguous()
     ref = oracle.attn_bwd(sl(q), sl(k), sl(v), sl(do), causal=True, scale=w.scale)
     for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
         gf = sl(got.cpu()).to(torch.float64).numpy()
+        worst = 0.0
         for i, bh in enumerate(heads):
             err = float(np.abs(gf[i] - want[i]).max())
             tol = bwd_tolerance(want[i], w.dtype)
-            say("  %s head %s: max|err| %.3g  max|ref| %.3g  tol %.3g"
-                % (name, bh, err, np.abs(want[i]).max(), tol))
+            worst = max(worst, err / tol)
             assert err <= tol, "head %s %s: max |err| %.3g > %.3g" % (bh, name, err, tol)
+        say("  %s over %d heads: worst max|err| / tol %.3f" % (name, len(heads), worst))
 
 
 def test_bwd_gqa_workload_full_size():
@@ -148,8 +155,9 @@ def test_bwd_gqa_workload_full_size():
     launch configuration the benchmark times, against the identity that holds at any
     size: with every K/V head repeated for its query heads the problem becomes MHA,
     whose dQ is the same and whose dK, dV summed over each group's heads are the
-    grouped dK, dV.  The MHA run takes the direct path (no partial sums); its
-    per-head gradients were checked against the oracle above."""
+    grouped dK, dV (the MHA run takes the direct path, no partial sums); and one
+    whole K/V-head group (its eight query heads' dQ, the shared dK, dV) against
+    the oracle."""
     w = W.lookup("bwd_gqa8_causal_bf16_b1_hq32_hkv4_s4096_d128")
     R = w.Hq // w.Hkv
     dev = torch.device("cuda:0")
@@ -175,3 +183,24 @@ def test_bwd_gqa_workload_full_size():
         say("  %s: max|grouped - summed MHA| %.3g  max|ref| %.3g  tol %.3g"
             % (name, err, np.abs(want).max(), tol))
         assert err <= tol, "%s: max |err| %.3g > %.3g" % (name, err, tol)
+    # one whole K/V-head group against the oracle: its R query heads run as R
+    # one-head problems on the shared K/V head (one oracle thread each); the group's
+    # dK, dV are the sums of theirs over the query heads (the gradient of a shared
+    # input), taken here in fp64
+    g = 1
+    hs = range(g * R, (g + 1) * R)
+    say("  K/V group %d (query heads %d..%d) against the oracle" % (g, hs[0], hs[-1]))
+    rep = lambda t: torch.cat([t[:, g:g + 1]] * R, dim=0).contiguous()
+    qs = torch.cat([q[:, h:h + 1] for h in hs], dim=0).contiguous()
+    dos = torch.cat([do[:, h:h + 1] for h in hs], dim=0).contiguous()
+    rq, rk, rv = oracle.attn_bwd(qs, rep(k), rep(v), dos, causal=True, scale=w.scale)
+    checks = (("dq", torch.cat([dq.cpu()[:, h:h + 1] for h in hs], dim=0), rq),
+              ("dk", dk.cpu()[:, g:g + 1], rk.sum(axis=0, keepdims=True)),
+              ("dv", dv.cpu()[:, g:g + 1], rv.sum(axis=0, keepdims=True)))
+    for name, got, want in checks:
+        gf = got.to(torch.float64).numpy()
+        err = float(np.abs(gf - want).max())
+        tol = bwd_tolerance(want, w.dtype)
+        say("  %s (group %d) vs oracle: max|err| %.3g  max|ref| %.3g  tol %.3g"
+            % (name, g, err, np.abs(want).max(), tol))
+        assert err <= tol, "group %d %s: max |err| %.3g > %.3g" % (g, name, err, tol)

@@ -3,11 +3,10 @@
 Every output element is compared on shapes with one or a few query rows per head:
 MHA, GQA, MQA, ragged chunk tails, Sq > 1 with the causal mask, Sq > Sk (rows with
 no visible key), explicit and automatic chunk counts, and the decode workload at
-full size (sampled rows).  The split and merge must give a deterministic result that
+full size (every element).  The split and merge must give a deterministic result that
 agrees with the prefill path to the stated tolerance."""
 import zlib
 
-import numpy as np
 import pytest
 import torch
 
@@ -80,18 +79,15 @@ def test_decode_deterministic_and_matches_prefill():
 
 
 @pytest.mark.parametrize("name", list(W.DECODE))
-def test_decode_workload_sampled(name):
-    """The decode workloads at full size: sampled rows against the oracle."""
+def test_decode_workload_whole_output(name):
+    """The decode workloads at full size: every element of O and the LSE against
+    the oracle (one query row per sequence and head, so the oracle takes under a
+    second)."""
     w = W.lookup(name)
-    say("case", name, "(full size)")
+    say("case", name, "(full size, every element)")
     q, k, v = W.make_inputs(w)
     o, lse = run_decode(q, k, v, w.causal, 0, scale=w.scale)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    rng = np.random.default_rng(w.seed)
-    total = w.B * w.Hq * w.Sq
-    rows = np.unique(np.concatenate([rng.integers(0, total, size=96), [0, total - 1]])).astype(np.int64)
-    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, rows=rows)
-    og = o.reshape(-1, w.D)[torch.from_numpy(rows)]
-    lg = lse.reshape(-1)[torch.from_numpy(rows)]
-    e = compare(og, lg, o_ref, lse_ref, w.dtype, name)
-    say("  %d rows: max|dO| %.3g  max|dLSE| %.3g" % (len(rows), *e))
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    e = compare(o, lse, o_ref, lse_ref, w.dtype, name)
+    say("  %s: every element, max|dO| %.4g  max|dLSE| %.4g" % (name, *e))

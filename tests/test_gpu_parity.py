@@ -1,8 +1,8 @@
 """Parity of the HIP path with the fp64 oracle, element by element (GPU).
 
-Small and ragged shapes compare every output element; the five named workloads
-and the attention variants at full size compare sampled rows (computed one by one by the oracle) and check
-properties of the whole output."""
+Small and ragged shapes, the five named workloads and the attention variants
+at full size compare every output element (O and LSE); the million-key case
+compares sampled rows the oracle computes one by one."""
 import zlib
 
 import numpy as np
@@ -54,7 +54,7 @@ def test_small_fp32_workload():
     check_full(W.WORKLOADS["mha_fp32_b1_h2_s128_d64"])
 
 
-@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5, 2.0])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5, 2.0, 1e-39])
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
 def test_other_scales(scale, dt):
     w = W.custom(dt, 1, 2, 1, 200, 333, 128, True, seed=77)
@@ -84,23 +84,21 @@ FULL = [n for n in W.ORDER if n != "mha_fp32_b1_h2_s128_d64"] + list(W.VARIANTS)
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def test_full_size_whole_output(name):
     """The named workloads and the attention variants (MQA, GQA-8, fp16) at full
-    size: sampled rows against the oracle, plus whole-output properties (every
-    value finite, every LSE finite since each query sees at least one key)."""
+    size, in the launch configuration the benchmark times: every element of O and
+    of the LSE against the oracle (which runs on all host cores: about 2 s for the
+    D = 64 workload, 15 s at S = 4096, 30 s for GQA at S = 8192 and 60 s at
+    S = 16384).  Also: rows of O lie inside the range of V (convex mixes)."""
     w = W.lookup(name)
-    say("case", name, "(full size)")
+    say("case", name, "(full size, every element)")
     q, k, v = W.make_inputs(w)
     o, lse = run_gpu(q, k, v, w.causal, scale=w.scale)
     assert torch.isfinite(o).all(), "non-finite O"
     assert torch.isfinite(lse).all(), "non-finite LSE"
-    rows = sample_rows(w, 160, seed=w.seed)
-    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, rows=rows)
-    og = o.reshape(-1, w.D)[torch.from_numpy(rows)]
-    lg = lse.reshape(-1)[torch.from_numpy(rows)]
-    e = compare(og, lg, o_ref, lse_ref, w.dtype, name)
-    say("  %d rows: max|dO| %.3g  max|dLSE| %.3g" % (len(rows), *e))
-    # whole-output property: rows of O lie inside the range of V (convex mixes)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    e = compare(o, lse, o_ref, lse_ref, w.dtype, name)
+    say("  %s: every element, max|dO| %.4g  max|dLSE| %.4g" % (name, *e))
     vmin = v.to(torch.float32).amin().item()
     vmax = v.to(torch.float32).amax().item()
     of = o.to(torch.float32)
