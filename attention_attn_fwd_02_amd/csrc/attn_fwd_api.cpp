@@ -78,16 +78,25 @@ size_t decode_workspace(int64_t rows, int D, int nsplit) {
     return (size_t)nsplit * (size_t)rows * ((size_t)D + 1) * sizeof(float);
 }
 
-// Parameters and launch of the prefill kernel (arguments already validated).
-// rope: 0, or the rotary layout with its tables (then k is the rotated copy).
-int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-               int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
-               int dtype, int rope, const float* rcos, const float* rsin, hipStream_t stream) {
+// Everything one prefill launch needs, decided on the host before anything is enqueued.
+struct FwdLaunch {
+    const void* fn;
+    unsigned nwg;
+    int threads;
+    attn_impl::AttnParams p;
+};
+
+// Kernel choice, scale folding and launch mapping of the prefill kernel (arguments
+// already validated).  rope: 0, or the rotary layout with its tables (then k is the
+// rotated copy).  Enqueues nothing, so every error is returned before any launch.
+int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+                int dtype, int rope, const float* rcos, const float* rsin, FwdLaunch* out) {
     using namespace attn_impl;
     const KernelChoice kc = select_kernel(dtype, D, causal ? 1 : 0, rope);
     if (!kc.fn) return ATTN_ERR_UNSUPPORTED;
 
-    AttnParams p;
+    AttnParams& p = out->p;
     p.rcos = rcos;
     p.rsin = rsin;
     p.q = q;
@@ -115,10 +124,15 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     while (gb * per_group < 64 && groups % (2 * gb) == 0) gb *= 2;
     p.gbundle = gb;
     p.xcd_remap = ((groups / gb) % 8 == 0) ? 1 : 0;
+    out->fn = kc.fn;
+    out->nwg = (unsigned)nwg;
+    out->threads = kc.threads;
+    return ATTN_OK;
+}
 
-    void* args[] = {&p};
-    const hipError_t err = hipLaunchKernel(kc.fn, dim3((unsigned)nwg), dim3(kc.threads), args, 0,
-                                           stream);
+int enqueue_fwd(FwdLaunch& L, hipStream_t stream) {
+    void* args[] = {&L.p};
+    const hipError_t err = hipLaunchKernel(L.fn, dim3(L.nwg), dim3(L.threads), args, 0, stream);
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -127,10 +141,13 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int Hq, int Hkv, int Sq, int Sk, int D,
                         float scale, int causal, int dtype, hipStream_t stream) {
-    const int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
+    int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
     if (st != ATTN_OK) return st;
-    return launch_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, 0, nullptr,
-                      nullptr, stream);
+    FwdLaunch L;
+    st = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, 0, nullptr,
+                     nullptr, &L);
+    if (st != ATTN_OK) return st;
+    return enqueue_fwd(L, stream);
 }
 
 extern "C" int attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -152,6 +169,12 @@ extern "C" int attn_fwd_rope(const void* q, const void* k, const void* v, void* 
 
     const void* rk = select_rope(dtype, D, rope_layout);
     if (!rk) return ATTN_ERR_UNSUPPORTED;
+    // the attention launch is fully decided (scale, kernel, grid) before the key
+    // pass is enqueued, so an error leaves k_rot and every output untouched
+    FwdLaunch L;
+    const int sp = prepare_fwd(q, k_rot, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype,
+                               rope_layout, rope_cos, rope_sin, &L);
+    if (sp != ATTN_OK) return sp;
     RopeParams rp;
     rp.x = k;
     rp.y = k_rot;
@@ -165,8 +188,7 @@ extern "C" int attn_fwd_rope(const void* q, const void* k, const void* v, void* 
     void* a1[] = {&rp};
     if (hipLaunchKernel(rk, dim3((unsigned)nblk), dim3(256), a1, 0, stream) != hipSuccess)
         return ATTN_ERR_LAUNCH;
-    return launch_fwd(q, k_rot, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype,
-                      rope_layout, rope_cos, rope_sin, stream);
+    return enqueue_fwd(L, stream);
 }
 
 extern "C" int attn_fwd_decode_workspace(int B, int Hq, int Hkv, int Sq, int Sk, int D, int nsplit,
@@ -183,26 +205,31 @@ extern "C" int attn_fwd_decode_workspace(int B, int Hq, int Hkv, int Sq, int Sk,
     return ATTN_OK;
 }
 
-extern "C" int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int Hq, int Hkv, int Sq, int Sk, int D,
-                               float scale, int causal, int dtype, int nsplit,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The split-KV pass and the merge.  The partial results go to `workspace` (at
+// least `workspace_bytes` bytes).
+int decode_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal, int dtype,
+                int nsplit, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     using namespace attn_impl;
     const int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
     if (st != ATTN_OK) return st;
     if (dtype == ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
     if ((int64_t)(Hq / Hkv) * Sq > 32) return ATTN_ERR_UNSUPPORTED;
+    DecodeParams dp;
+    fold_scale(scale, &dp.c, &dp.q_mode);
+    if (!(dp.c > 0.0f) || !isfinite(dp.c)) return ATTN_ERR_INVALID_ARG;
     const DecodePlan pl = decode_plan(B, Hkv, Sk, nsplit);
     const int64_t rows = (int64_t)B * Hq * Sq;
     const size_t need = decode_workspace(rows, D, pl.nsplit);
-    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
     const int64_t nwg = (int64_t)B * Hkv * pl.nsplit;
     if (nwg > INT32_MAX || rows > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
     const void* fs = select_decode_split(dtype, D, causal ? 1 : 0);
     const void* fm = select_decode_merge(dtype, D);
     if (!fs || !fm) return ATTN_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
 
-    DecodeParams dp;
     dp.q = q;
     dp.k = k;
     dp.v = v;
@@ -213,8 +240,6 @@ extern "C" int attn_fwd_decode(const void* q, const void* k, const void* v, void
     dp.Hkv = Hkv;
     dp.Sq = Sq;
     dp.Sk = Sk;
-    fold_scale(scale, &dp.c, &dp.q_mode);
-    if (!(dp.c > 0.0f) || !isfinite(dp.c)) return ATTN_ERR_INVALID_ARG;
     dp.chunk = pl.chunk;
     dp.nsplit = pl.nsplit;
     void* a1[] = {&dp};
@@ -232,6 +257,16 @@ extern "C" int attn_fwd_decode(const void* q, const void* k, const void* v, void
     if (hipLaunchKernel(fm, dim3((unsigned)rows), dim3(D), a2, 0, stream) != hipSuccess)
         return ATTN_ERR_LAUNCH;
     return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                               float scale, int causal, int dtype, int nsplit,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, nsplit,
+                       workspace, workspace_bytes, stream);
 }
 
 namespace {
@@ -326,7 +361,12 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.Sq = Sq;
     p.Sk = Sk;
     p.c = (float)((double)scale * 1.4426950408889634);
-    p.ce = p.c != 0.f ? p.c : 0x1p-100f;
+    // The dK/dV pass starts its score accumulators at -LSE2/ce and multiplies by ce:
+    // below 2^-100 in magnitude the scores' contribution c.s is far under one ulp of
+    // LSE2, so ce = 2^-100 (which keeps -LSE2/ce finite) gives the same fp32 weights
+    // exp2(-LSE2); a zero or tiny scale thus never overflows the start value.
+    p.ce = fabsf(p.c) >= 0x1p-100f ? p.c : 0x1p-100f;
+    if (!isfinite(p.c)) return ATTN_ERR_INVALID_ARG;   // |scale| * log2(e) past the fp32 range
     p.scale = scale;
     p.rows = rows;
     void* args[] = {&p};

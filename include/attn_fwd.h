@@ -56,8 +56,10 @@ typedef enum {
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = 1,   /* a null or misaligned pointer, a size < 1, Hq % Hkv != 0,
-                                   a non-finite scale, an unknown dtype, or sizes whose
-                                   element counts overflow 64-bit offsets */
+                                   a non-finite scale or one whose magnitude times log2(e)
+                                   leaves the fp32 range (|scale| above about 2.36e38),
+                                   an unknown dtype, or sizes whose element counts
+                                   overflow 64-bit offsets */
     ATTN_ERR_UNSUPPORTED = 2,   /* a head dimension D other than 64 or 128, a grid too
                                    large for one launch, or one (batch, head) slice of
                                    q, k or v of 2 GiB - 1 MiB or more */
@@ -77,7 +79,8 @@ typedef enum {
  *                           in which case no log-sum-exp is written
  *   B, Hq, Hkv, Sq, Sk      sizes, each >= 1; Hq must be a multiple of Hkv
  *   D                       head dimension: 64 or 128
- *   scale                   any finite value (1/sqrt(D) is the usual choice)
+ *   scale                   any finite value with |scale| * log2(e) inside the fp32
+ *                           range (1/sqrt(D) is the usual choice)
  *   causal                  0: every key is visible; otherwise the bottom-right
  *                           causal mask described above
  *   dtype                   an attn_dtype_t
@@ -142,6 +145,7 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
                     float scale, int causal, int dtype, int nsplit,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 
 /*
  * Gradients of attn_fwd (the FlashAttention backward the FIBER page evaluates as
@@ -210,7 +214,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * dtype must be ATTN_BF16 or ATTN_FP16 (ATTN_FP32: ATTN_ERR_UNSUPPORTED).  Errors
  * are those of attn_fwd, plus ATTN_ERR_INVALID_ARG for a null or misaligned k_rot
  * or table, an unknown layout, or Sq > Sk (queries would sit at negative
- * positions).  Deterministic; nothing is allocated.
+ * positions).  Every check, the attention launch's included, is made before the
+ * key pass is enqueued: on any error nothing is enqueued and k_rot, o and lse are
+ * untouched.  Deterministic; nothing is allocated.
  */
 typedef enum {
     ATTN_ROPE_INTERLEAVED = 1,

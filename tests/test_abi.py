@@ -36,8 +36,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"attn_fwd", "attn_status_str", "attn_fwd_decode",
-                          "attn_fwd_decode_workspace", "attn_bwd", "attn_bwd_workspace",
-                          "attn_fwd_rope"}, names
+                          "attn_fwd_decode_workspace", "attn_bwd",
+                          "attn_bwd_workspace", "attn_fwd_rope"}, names
     raw = ctypes.CDLL(A.LIB_PATH)
     for nm in names:
         assert hasattr(raw, nm), nm
@@ -82,6 +82,7 @@ INVALID = [
     dict(B=-1), dict(Sq=-5), dict(Sk=-1),
     dict(Hq=6, Hkv=4), dict(Hq=3, Hkv=2),
     dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=float("-inf")),
+    dict(scale=3e38), dict(scale=-2.4e38),     # |scale| * log2(e) past the fp32 range
     dict(dtype=3), dict(dtype=-1),
     dict(q=Q + 8), dict(k=K + 2), dict(v=V + 4), dict(o=O + 1), dict(lse=L + 2),
     dict(B=1 << 20, Hq=1 << 20, Hkv=1 << 20, Sq=1 << 20, D=128),   # 2^67 elements
@@ -172,6 +173,7 @@ DINVALID = [
     dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(B=0), dict(Sk=0),
     dict(Hq=6, Hkv=4), dict(scale=float("nan")), dict(dtype=7), dict(q=Q + 2), dict(lse=L + 1),
     dict(ws=None), dict(ws=W_ADDR + 8), dict(ws_bytes=0), dict(ws_bytes=1000),
+    dict(scale=3e38),
 ]
 
 
@@ -236,7 +238,8 @@ BINVALID = [
     dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(do=None),
     dict(dq=None), dict(dk=None), dict(dv=None), dict(do=DO_ + 8), dict(dq=DQ_ + 2),
     dict(dk=DK_ + 4), dict(dv=DV_ + 1), dict(lse=L + 2), dict(Hq=3, Hkv=2), dict(Sk=0),
-    dict(scale=float("inf")), dict(dtype=5), dict(ws=None), dict(ws=W_ADDR + 4),
+    dict(scale=float("inf")), dict(scale=3e38), dict(scale=-2.4e38), dict(dtype=5),
+    dict(ws=None), dict(ws=W_ADDR + 4),
     dict(ws_bytes=64 * 4 * 12 - 1), 
     dict(ws_bytes=3072 + 2 * 2 * 2 * 64 * 128 * 4 - 1),   # short by one byte of the partial sums
 ]
@@ -272,6 +275,9 @@ RINVALID = [
     dict(q=None), dict(k=None), dict(o=None), dict(kr=None), dict(rc=None), dict(rs=None),
     dict(kr=KR_ + 2), dict(rc=RC_ + 4), dict(rs=RS_ + 8), dict(layout=0), dict(layout=3),
     dict(Sq=65), dict(Hq=3, Hkv=2), dict(B=0), dict(scale=float("nan")), dict(dtype=9),
+    # caught by the attention launch's own preparation, which runs before the key
+    # pass is enqueued (so nothing is launched and k_rot is untouched)
+    dict(scale=3e38), dict(scale=-2.4e38),
 ]
 
 
@@ -284,6 +290,12 @@ def test_rope_invalid_arguments(lib, bad):
                          ids=["fp32", "d96", "d256"])
 def test_rope_unsupported(lib, bad):
     assert _rcall(**bad) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_rope_grid_too_large_is_unsupported(lib):
+    # 2^42 attention workgroups: refused by the attention launch's preparation,
+    # before the key pass is enqueued
+    assert _rcall(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Sq=1 << 20, Sk=1 << 20) == A.ATTN_ERR_UNSUPPORTED
 
 
 def test_rope_binding_refuses_host_tensors():
