@@ -4,16 +4,25 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 A step is one `attn_fwd` call over the whole workload (default: bf16, causal,
-B = 2, H = 32, S = 4096, D = 128) with Q, K, V already resident in HBM.  After W
-untimed steps, exactly K steps are timed between two device synchronisations.
-One JSON line goes to stdout; progress goes to stderr.
+B = 2, H = 32, S = 4096, D = 128) with Q, K, V already resident in HBM.  First an
+untimed clock-settle phase runs steps for a fixed wall time (`--settle-s`, 1 s by
+default: from idle the GPU boosts, then drops under the power limit and takes about
+50 ms to reach its steady clock); then W untimed warm-up steps; then exactly K steps
+are timed between two device synchronisations.  One JSON line goes to stdout;
+progress goes to stderr.
 
 The line carries:
   value / ms_per_step   whole-job TFLOP/s (4*D FLOPs per visible query-key pair)
   roofline              the attention kernel against the dense bf16 MFMA peak, its
-                        average duration measured with HIP events on the launch stream;
+                        average duration measured with HIP events on the launch stream
+                        over the K timed steps; the K steps are also cut into five
+                        consecutive windows, each timed by its own events, and their
+                        median per-launch time is reported beside the mean;
                         `traffic` is the HBM bytes per launch from the committed
                         counter summary when it matches the current kernel source
+  clock                 the shader clock the driver reports while the timed steps run
+                        (pp_dpm_sclk's current level, a smoothed value), the settle
+                        phase's length, and the dense bf16 peak at that clock
   cpu_baseline          the fp64 CPU oracle timed on a bounded sample of the same
                         workload on this host (a reported baseline, not a target)
 
@@ -73,6 +82,96 @@ def committed_traffic(workload: str, prefix: str = "attn_fwd", src: str = KERNEL
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class SclkSampler:
+    """Samples the current shader clock the amdgpu driver reports (the line marked
+    '*' in pp_dpm_sclk, in MHz) every 10 ms on a background thread."""
+
+    def __init__(self):
+        import glob
+        files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = files[0] if files else None
+        self.values = []
+        self._stop = False
+        self._th = None
+
+    def _read(self):
+        for line in open(self.path):
+            if line.rstrip().endswith("*"):
+                tok = line.split(":", 1)[1].strip().split()[0].lower()
+                return float(tok.replace("mhz", ""))
+        return None
+
+    def start(self):
+        import threading
+        if self.path is None:
+            return self
+
+        def run():
+            while not self._stop:
+                try:
+                    v = self._read()
+                    if v is not None:
+                        self.values.append(v)
+                except (OSError, ValueError, IndexError):
+                    pass
+                time.sleep(0.01)
+        self._th = threading.Thread(target=run, daemon=True)
+        self._th.start()
+        return self
+
+    def stop(self):
+        self._stop = True
+        if self._th is not None:
+            self._th.join()
+        if not self.values:
+            try:
+                v = self._read() if self.path else None
+                if v is not None:
+                    self.values.append(v)
+            except (OSError, ValueError, IndexError):
+                pass
+        return self
+
+    def summary(self):
+        if not self.values:
+            return None
+        v = sorted(self.values)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1],
+                "samples": len(v), "source": "pp_dpm_sclk (driver-smoothed current level)"}
+
+
+def timed_run(step, steps, stream, torch):
+    """Exactly `steps` calls of `step` between two device synchronisations, cut
+    into (up to) five consecutive windows, each bracketed by HIP events on the
+    launch stream.  Returns (wall ms per step, event ms per launch over all steps,
+    the windows' per-launch event ms)."""
+    nwin = min(5, steps)
+    sizes = [steps // nwin + (1 if i < steps % nwin else 0) for i in range(nwin)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i, n in enumerate(sizes):
+        for _ in range(n):
+            step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wins = [evs[i].elapsed_time(evs[i + 1]) / n for i, n in enumerate(sizes)]
+    total = evs[0].elapsed_time(evs[-1]) / steps
+    return (t1 - t0) * 1e3 / steps, total, wins
+
+
 def copy_calibration(mib: int, steps: int):
     import torch
     n = mib * (1 << 20) // 4
@@ -116,13 +215,13 @@ def cpu_baseline(w, q, k, v, target_s: float):
     dt = time.perf_counter() - t0
     flops = 4.0 * w.D * pairs(rows)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d uniformly drawn query rows (seed 12345) of the %d rows, each over all "
                       "its visible keys; fp64; %.1f s; FLOPs = 4*D per visible pair"
                       % (n, total, dt)}
 
 
-def decode_line(args, w, name, wall_ms, kern_ms):
+def decode_line(args, w, name, wall_ms, kern_ms, med_ms, clock):
     """JSON line of a decode workload: bound by HBM bytes (K and V read once, Q read
     and O, LSE written once), so the figure is GB/s against the 8 TB/s peak.  The
     timed step is both kernels (split-KV pass and merge); the partial results they
@@ -149,7 +248,9 @@ def decode_line(args, w, name, wall_ms, kern_ms):
                      "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": committed_traffic(name, "attn_decode",
                                                   os.path.join(CSRC, "attn_decode_kernels.hip")),
-                     "kernel_ms_per_launch": round(kern_ms, 5)},
+                     "kernel_ms_per_launch": round(kern_ms, 5),
+                     "kernel_ms_median_of_5": round(med_ms, 5)},
+        "clock": clock,
         "cpu_baseline": None,
     }
 
@@ -159,6 +260,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed clock-settle phase before the warm-up, in seconds of wall time")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -229,32 +332,41 @@ def main():
         def step():
             fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
 
+    # clock settle: whole steps for a fixed wall time (checked every 16 steps)
+    settle_steps = 0
+    t_end = time.perf_counter() + max(0.0, args.settle_s)
+    while time.perf_counter() < t_end:
+        for _ in range(16):
+            step()
+        settle_steps += 16
+        torch.cuda.synchronize()
+    log("clock settle: %d steps in %.2f s" % (settle_steps, args.settle_s))
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log("warmup done (%d steps)" % args.warmup)
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    sampler = SclkSampler().start()
+    wall_ms, kern_ms, wins = timed_run(step, args.steps, stream, torch)
+    sampler.stop()
+    med_ms = sorted(wins)[len(wins) // 2]
     flops = W.bwd_flops(w) if backward else w.flops()
     value = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    log("timed %d steps: %.3f ms/step wall, %.3f ms/launch (events), %.1f TFLOP/s"
-        % (args.steps, wall_ms, kern_ms, achieved))
+    sclk = sampler.summary()
+    clock = {"settle_s": args.settle_s, "settle_steps": settle_steps, "sclk": sclk}
+    if sclk and w.dtype in ("bf16", "fp16"):
+        # dense 16-bit MFMA: 4096 FLOP per CU per clock
+        clock["bf16_peak_at_sclk_tflops"] = round(
+            props.multi_processor_count * 4096 * sclk["median_mhz"] * 1e6 / 1e12, 1)
+    log("timed %d steps: %.3f ms/step wall, %.4f ms/launch (events; windows %s), %.1f TFLOP/s, sclk %s"
+        % (args.steps, wall_ms, kern_ms, " ".join("%.4f" % x for x in wins), achieved,
+           sclk["median_mhz"] if sclk else "n/a"))
 
     if decode:
-        print(json.dumps(decode_line(args, w, name, wall_ms, kern_ms)), flush=True)
+        print(json.dumps(decode_line(args, w, name, wall_ms, kern_ms, med_ms, clock)), flush=True)
         return
 
     cpu = None
@@ -287,7 +399,9 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": (committed_traffic(name, "attn_bwd", os.path.join(CSRC, "attn_bwd_kernels.hip"))
                                  if backward else committed_traffic(name)),
-                     "kernel_ms_per_launch": round(kern_ms, 5)},
+                     "kernel_ms_per_launch": round(kern_ms, 5),
+                     "kernel_ms_median_of_5": round(med_ms, 5)},
+        "clock": clock,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
