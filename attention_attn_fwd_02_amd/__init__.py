@@ -12,11 +12,13 @@ does not touch the GPU.
 from .attn import (ATTN_BF16, ATTN_FP16, ATTN_FP32, ATTN_OK, ATTN_ERR_INVALID_ARG,
                    ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH, ATTN_ROPE_INTERLEAVED, ATTN_ROPE_HALVES,
                    AttnError, attn_bwd, attn_bwd_workspace, attn_fwd, attn_fwd_decode,
-                   attn_fwd_decode_workspace, attn_fwd_rope, attn_status_str, bwd, fwd,
-                   fwd_decode, fwd_rope, load_library)
+                   attn_fwd_decode_noalloc, attn_fwd_decode_workspace, attn_fwd_rope,
+                   attn_status_str, bwd, fwd, fwd_decode, fwd_decode_noalloc, fwd_rope,
+                   load_library)
 
 __all__ = ["ATTN_BF16", "ATTN_FP16", "ATTN_FP32", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_ROPE_INTERLEAVED", "ATTN_ROPE_HALVES",
            "AttnError", "attn_bwd", "attn_bwd_workspace", "attn_fwd", "attn_fwd_decode",
-           "attn_fwd_decode_workspace", "attn_fwd_rope", "attn_status_str", "bwd", "fwd",
-           "fwd_decode", "fwd_rope", "load_library"]
+           "attn_fwd_decode_noalloc", "attn_fwd_decode_workspace", "attn_fwd_rope",
+           "attn_status_str", "bwd", "fwd", "fwd_decode", "fwd_decode_noalloc", "fwd_rope",
+           "load_library"]

@@ -1,7 +1,7 @@
 """Thin Python binding of the C-ABI library `libattn_fwd.so` (include/attn_fwd.h).
 
 Argument marshalling only: every step runs in the HIP kernels behind `attn_fwd`,
-`attn_fwd_decode`, `attn_bwd` and `attn_fwd_rope`.  PyTorch supplies device memory and the stream.  If
+`attn_fwd_decode` (and its allocation-free variant), `attn_bwd` and `attn_fwd_rope`.  PyTorch supplies device memory and the stream.  If
 the library is missing this module raises; there is no fallback path.
 """
 import ctypes
@@ -47,6 +47,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                     i32, vp, sz, vp]
     lib.attn_fwd_decode.restype = i32
+    lib.attn_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                            i32, i32, i32, vp]
+    lib.attn_fwd_decode_noalloc.restype = i32
     lib.attn_bwd_workspace.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.attn_bwd_workspace.restype = i32
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
@@ -78,6 +81,14 @@ def attn_fwd_decode(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype
     return load_library().attn_fwd_decode(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
                                           int(causal), int(dtype), int(nsplit), workspace,
                                           int(workspace_bytes), stream)
+
+
+def attn_fwd_decode_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, nsplit,
+                            stream) -> int:
+    """The C entry point with raw integer pointers; returns the status code."""
+    return load_library().attn_fwd_decode_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D,
+                                                  float(scale), int(causal), int(dtype),
+                                                  int(nsplit), stream)
 
 
 def attn_bwd_workspace(B, Hq, Hkv, Sq, Sk, D):
@@ -207,6 +218,32 @@ def fwd_decode(q, k, v, causal=False, scale=None, nsplit=0, out=None, lse=None, 
                          lse.data_ptr() if want_lse else None, B, Hq, Hkv, Sq, Sk, D, scale,
                          causal, _dtype_code(q.dtype), nsplit, workspace.data_ptr(),
                          workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, (lse if want_lse else None)
+
+
+def fwd_decode_noalloc(q, k, v, causal=False, scale=None, nsplit=0, out=None, lse=None,
+                       want_lse=True, stream=None):
+    """`fwd_decode` through the allocation-free entry point: the partial results go
+    to the library's static 16 MiB device scratch instead of a workspace.  With
+    `out` (and `lse`) given, nothing is allocated here either."""
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _check_inputs(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_buffer(out, "out", q.shape, q.dtype, q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _check_buffer(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_fwd_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if want_lse else None, B, Hq, Hkv, Sq, Sk, D,
+                                 scale, causal, _dtype_code(q.dtype), nsplit, stream.cuda_stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return out, (lse if want_lse else None)

@@ -31,8 +31,16 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "attn_fwd_internal.h"
 #include "attn_kernel_common.h"
+
+// Scratch of the allocation-free decode entry point: the chunks' partial results
+// (O and LSE per chunk and query row) of one call.  Every GPU the library runs on
+// holds its own copy until the process ends; calls on one GPU share it.
+static __device__ __align__(256) uint8_t scratch[attn_impl::DECODE_SCRATCH_BYTES];
 
 namespace attn_impl {
 
@@ -298,6 +306,34 @@ __global__ __launch_bounds__(128) void attn_decode_merge(MergeParams p) {
         *out = __builtin_bit_cast(uint16_t, v);
     }
     if (p.lse && d == 0) p.lse[row] = (sum > 0.f) ? mx + logf(sum) : NEG_INF;
+}
+
+// Device address of this GPU's `scratch`, looked up once per device (with that
+// device current) and kept: host code never passes the array's name itself,
+// which on the host is only a stand-in for the symbol.
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::atomic<void*> scratch_ptr[SCRATCH_MAX_DEVICES];
+std::mutex scratch_mutex;
+}  // namespace
+
+int decode_scratch(void** ptr, size_t* bytes) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return 1;
+    void* a = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!a) {
+        std::lock_guard<std::mutex> lock(scratch_mutex);
+        a = scratch_ptr[dev].load(std::memory_order_acquire);
+        if (!a) {
+            void* q = nullptr;
+            if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return 1;
+            scratch_ptr[dev].store(q, std::memory_order_release);
+            a = q;
+        }
+    }
+    *ptr = a;
+    *bytes = DECODE_SCRATCH_BYTES;
+    return 0;
 }
 
 template <int DT, int D>

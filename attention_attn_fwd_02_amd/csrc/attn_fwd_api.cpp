@@ -208,10 +208,13 @@ extern "C" int attn_fwd_decode_workspace(int B, int Hq, int Hkv, int Sq, int Sk,
 namespace {
 
 // The split-KV pass and the merge.  The partial results go to `workspace` (at
-// least `workspace_bytes` bytes).
+// least `workspace_bytes` bytes), or with `scratch_call` to the library's static
+// device scratch (the workspace arguments are then ignored, and a call whose
+// partial results would not fit it is refused).
 int decode_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal, int dtype,
-                int nsplit, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                int nsplit, void* workspace, size_t workspace_bytes, bool scratch_call,
+                hipStream_t stream) {
     using namespace attn_impl;
     const int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, dtype);
     if (st != ATTN_OK) return st;
@@ -228,6 +231,11 @@ int decode_impl(const void* q, const void* k, const void* v, void* o, float* lse
     const void* fs = select_decode_split(dtype, D, causal ? 1 : 0);
     const void* fm = select_decode_merge(dtype, D);
     if (!fs || !fm) return ATTN_ERR_UNSUPPORTED;
+    // every check above is made before the scratch lookup (the first runtime call)
+    if (scratch_call) {
+        if (need > DECODE_SCRATCH_BYTES) return ATTN_ERR_UNSUPPORTED;
+        if (decode_scratch(&workspace, &workspace_bytes) != 0) return ATTN_ERR_LAUNCH;
+    }
     if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
 
     dp.q = q;
@@ -266,7 +274,15 @@ extern "C" int attn_fwd_decode(const void* q, const void* k, const void* v, void
                                float scale, int causal, int dtype, int nsplit,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, nsplit,
-                       workspace, workspace_bytes, stream);
+                       workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                       float scale, int causal, int dtype, int nsplit,
+                                       hipStream_t stream) {
+    return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, dtype, nsplit,
+                       nullptr, 0, true, stream);
 }
 
 namespace {

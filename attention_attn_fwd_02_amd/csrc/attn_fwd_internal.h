@@ -3,6 +3,7 @@
 #ifndef ATTN_FWD_INTERNAL_H
 #define ATTN_FWD_INTERNAL_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #define ATTN_IMPL_BF16 0
@@ -104,6 +105,13 @@ BwdKernels select_bwd(int dtype, int D, int causal);   // null members: unsuppor
 
 const void* select_decode_split(int dtype, int D, int causal);   // null: unsupported
 const void* select_decode_merge(int dtype, int D);
+
+// Bytes of the static device scratch that the allocation-free decode entry point
+// uses for the chunks' partial results (16 MiB).
+constexpr size_t DECODE_SCRATCH_BYTES = (size_t)16 << 20;
+// Device address and size of the current device's scratch (looked up once per
+// device and cached); 0 on success, nonzero when the runtime cannot provide it.
+int decode_scratch(void** ptr, size_t* bytes);
 
 }  // namespace attn_impl
 

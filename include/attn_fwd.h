@@ -146,6 +146,28 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int causal, int dtype, int nsplit,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * attn_fwd_decode_noalloc -- attn_fwd_decode for callers that cannot allocate
+ * device memory or bring a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * Same arguments, kernels and results as attn_fwd_decode (bit for bit), without
+ * the workspace: the chunks' partial results go to a static device array of
+ * 16 MiB (ATTN_DECODE_SCRATCH_BYTES) inside the library, one per GPU, held until
+ * the process ends.  Calls whose partial results would not fit (the size
+ * attn_fwd_decode_workspace reports exceeds it) return ATTN_ERR_UNSUPPORTED.  The
+ * first call on a device looks up that device's copy of the array (a runtime
+ * query, no allocation; make it outside graph capture); ATTN_ERR_LAUNCH if the
+ * runtime cannot provide it.  Nothing is allocated, no memset or copy is issued.
+ * Every call on one GPU shares the array: calls that may overlap on one GPU
+ * (different streams without ordering between them) race and give wrong results;
+ * calls on one stream are ordered and safe.  Other errors are those of
+ * attn_fwd_decode (minus the workspace checks).
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                            float scale, int causal, int dtype, int nsplit, hipStream_t stream);
 
 /*
  * Gradients of attn_fwd (the FlashAttention backward the FIBER page evaluates as

@@ -36,7 +36,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"attn_fwd", "attn_status_str", "attn_fwd_decode",
-                          "attn_fwd_decode_workspace", "attn_bwd",
+                          "attn_fwd_decode_workspace", "attn_fwd_decode_noalloc", "attn_bwd",
                           "attn_bwd_workspace", "attn_fwd_rope"}, names
     raw = ctypes.CDLL(A.LIB_PATH)
     for nm in names:
@@ -180,6 +180,41 @@ DINVALID = [
 @pytest.mark.parametrize("bad", DINVALID, ids=[str(b) for b in DINVALID])
 def test_decode_invalid_arguments(lib, bad):
     assert _dcall(**bad) == A.ATTN_ERR_INVALID_ARG
+
+
+def _ncall(**kw):
+    a = dict(DGOOD)
+    a.update(kw)
+    return A.attn_fwd_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                     a["Hkv"], a["Sq"], a["Sk"], a["D"], a["scale"], a["causal"],
+                                     a["dtype"], a["nsplit"], a["stream"])
+
+
+NINVALID = [d for d in DINVALID if not (set(d) & {"ws", "ws_bytes"})]
+
+
+@pytest.mark.parametrize("bad", NINVALID, ids=[str(b) for b in NINVALID])
+def test_decode_noalloc_invalid_arguments(lib, bad):
+    assert _ncall(**bad) == A.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(dtype=A.ATTN_FP32), dict(D=96), dict(Hq=64, Hkv=1),
+                                 dict(Sq=5, Hq=8, Hkv=1),
+                                 # 128 chunks x 256 rows x 129 floats: 16.9 MB > 16 MiB scratch
+                                 dict(B=8, Hq=32, Hkv=8, Sq=1, Sk=4096, nsplit=128)],
+                         ids=["fp32", "d96", "mqa64", "rows40", "past_scratch"])
+def test_decode_noalloc_unsupported(lib, bad):
+    assert _ncall(**bad) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_decode_noalloc_scratch_limit_matches_header(lib):
+    text = open(HEADER).read()
+    assert "#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    # the largest call that fits: 4 chunks x 8128 rows x 129 floats <= 16 MiB
+    st, need = A.attn_fwd_decode_workspace(254, 32, 32, 1, 1024, 128, 4)
+    assert st == A.ATTN_OK and need <= 16 << 20
+    st, need = A.attn_fwd_decode_workspace(8, 32, 8, 1, 4096, 128, 128)
+    assert st == A.ATTN_OK and need > 16 << 20
 
 
 @pytest.mark.parametrize("bad", [dict(dtype=A.ATTN_FP32), dict(D=96), dict(Hq=64, Hkv=1),
