@@ -148,12 +148,19 @@ __device__ __forceinline__ int tr_lane_base(int lane, int tpitch) {
 // Workgroup w -> (group, block).  When the groups split evenly over the 8 XCDs
 // (the dispatcher sends workgroup w to XCD w % 8), all blocks of a group run on one
 // XCD, so the group's streamed operands (Q and dO, or K and V) stay in that XCD's
-// L2.  Blocks of a group are dispatched in order of their index.
+// L2.  With fewer groups than XCDs (a divisor of 8, e.g. the dQ pass of a shape with
+// four K/V heads), each group gets 8 / ngrp XCDs of its own, its blocks dealt over
+// them in turn, so that each XCD still streams a single group's operands.  Blocks
+// of a group are dispatched in order of their index.
 __device__ __forceinline__ void bwd_map(int w, int nblk, int ngrp, int& grp, int& blk) {
+    const int xcd = w & 7, slot = w >> 3;
     if (ngrp % 8 == 0) {
-        const int xcd = w & 7, slot = w >> 3;
         grp = 8 * (slot / nblk) + xcd;
         blk = slot % nblk;
+    } else if (8 % ngrp == 0 && nblk % (8 / ngrp) == 0) {
+        const int x = 8 / ngrp;                 // XCDs per group
+        grp = xcd / x;
+        blk = slot * x + xcd % x;
     } else {
         grp = w / nblk;
         blk = w % nblk;
