@@ -256,6 +256,7 @@ void attn_fwd_16(AttnParams p) {
     // per query (this lane's column): reference m (log2 domain) and the partial sum
     // of this half-wave's weights, in fp32
     float m_run = NEG_INF, le_run = 0.f;
+    float neg_m = -0.f;     // -m_run, or 0 while m_run is -inf (the weights' offset)
 
     // ---- DMA lane offsets (loop-invariant): DMA instruction i of this wave fills
     // LDS slots 64*(wave + NW*i) + lane; a slot is (row, chunk) of the padded tile,
@@ -348,6 +349,7 @@ void attn_fwd_16(AttnParams p) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
         m_run = m_new;
+        neg_m = (m_new == NEG_INF) ? 0.f : -m_new;
         le_run *= alpha;
 #pragma unroll
         for (int d = 0; d < DBLK; ++d)
@@ -356,12 +358,11 @@ void attn_fwd_16(AttnParams p) {
     };
     // ---- weights of one 32-key block, packed to 16 bits; returns their fp32 sum
     auto weights = [&](const f32x16& s, uint32_t (&pk)[8]) -> float {
-        const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
         float se[4];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(fmaf(s[r], p.c, -m_use));
-            const float p1 = fast_exp2(fmaf(s[r + 1], p.c, -m_use));
+            const float p0 = fast_exp2(fmaf(s[r], p.c, neg_m));
+            const float p1 = fast_exp2(fmaf(s[r + 1], p.c, neg_m));
             if (r < 4) {
                 se[r] = p0;
                 se[r + 1] = p1;
