@@ -285,11 +285,31 @@ __global__ __launch_bounds__(128) void attn_decode_merge(MergeParams p) {
     const int64_t row = blockIdx.x;
     const int d = threadIdx.x;
     const int64_t rows = p.rows;
+    const int ns = p.nsplit;
+    // the first MS partials are loaded together, before the maximum is known (one
+    // memory round trip); missing ones read as an empty chunk (LSE -inf, O 0), which
+    // changes neither the maximum nor the sums
+    constexpr int MS = 8;
+    float lv[MS], ov[MS];
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+        const bool live = s < ns;
+        lv[s] = live ? p.lpart[(int64_t)s * rows + row] : NEG_INF;
+        ov[s] = live ? p.opart[((int64_t)s * rows + row) * D + d] : 0.f;
+    }
     float mx = NEG_INF;
-    for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, p.lpart[(int64_t)s * rows + row]);
+#pragma unroll
+    for (int s = 0; s < MS; ++s) mx = fmaxf(mx, lv[s]);
+    for (int s = MS; s < ns; ++s) mx = fmaxf(mx, p.lpart[(int64_t)s * rows + row]);
     float sum = 0.f, acc = 0.f;
     if (mx != NEG_INF) {
-        for (int s = 0; s < p.nsplit; ++s) {
+#pragma unroll
+        for (int s = 0; s < MS; ++s) {
+            const float w = (lv[s] == NEG_INF) ? 0.f : expf(lv[s] - mx);
+            sum += w;
+            acc += w * ov[s];
+        }
+        for (int s = MS; s < ns; ++s) {
             const float l = p.lpart[(int64_t)s * rows + row];
             const float w = (l == NEG_INF) ? 0.f : expf(l - mx);
             sum += w;
