@@ -13,6 +13,13 @@
 namespace attn_impl {
 
 // Everything a kernel needs, passed by value as its only argument.
+// Division by a launch constant d >= 1 of a non-negative n < 2^31 as a multiply and a
+// shift: n / d = (n * m) >> s with s = 31 + ceil(log2 d), m = ceil(2^s / d) < 2^32
+// (the round-up method of Granlund and Montgomery, "Division by invariant integers
+// using multiplication", PLDI 1994: m*d - 2^s < d <= 2^ceil(log2 d), so the product
+// overshoots n/d by less than 1/d and the floor is exact).
+struct FastDiv { uint32_t m, s; };
+
 struct AttnParams {
     const void* q;
     const void* k;
@@ -24,7 +31,12 @@ struct AttnParams {
     int q_mode;       // 0: use Q as is; 1: use -Q (negative scale); 2: use 0 (zero scale)
     int nq;           // query tiles per head
     int xcd_remap;    // 1: give each XCD whole bundles of key/value-head groups
-    int gbundle;      // key/value-head groups per bundle (divides B * Hkv)
+    int gbundle;      // key/value-head groups per bundle (divides B * Hkv), a power of two
+    int R;            // query heads per key/value head, Hq / Hkv
+    FastDiv div_bu;   // by the workgroups per bundle, gbundle * R * nq
+    FastDiv div_gr;   // by gbundle * R
+    FastDiv div_r;    // by R
+    FastDiv div_hkv;  // by Hkv
     const float* rcos;  // rotary embedding tables [Sk][D/2] (kernels built with it only)
     const float* rsin;
 };

@@ -55,26 +55,33 @@ namespace attn_impl {
 // evenly over the 8 XCDs (workgroup w is dispatched to XCD w % 8), each XCD gets
 // whole bundles, so every query tile and query head that reads one K/V head runs
 // on the XCD that caches it.
-struct TileCoord { int b, hq, qt; };
+struct TileCoord { int b, hq, kvh, qt; };
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (uint32_t)(((uint64_t)n * f.m) >> f.s);
+}
 __device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
-    const int R = p.Hq / p.Hkv;      // query heads per key/value head
-    const int G = p.gbundle;         // key/value-head groups per bundle
-    const int BU = G * R * p.nq;     // workgroups per bundle
-    int bundle, u;
+    const uint32_t R = p.R;              // query heads per key/value head
+    const uint32_t G = p.gbundle;        // key/value-head groups per bundle
+    const uint32_t BU = G * R * p.nq;    // workgroups per bundle
+    uint32_t bundle, u;
     if (p.xcd_remap) {
-        const int xcd = w & 7, slot = w >> 3;
-        bundle = xcd + 8 * (slot / BU);
-        u = slot % BU;
+        const uint32_t xcd = w & 7, slot = (uint32_t)w >> 3;
+        const uint32_t k = fdiv(slot, p.div_bu);
+        bundle = xcd + 8 * k;
+        u = slot - k * BU;
     } else {
-        bundle = w / BU;
-        u = w % BU;
+        bundle = fdiv(w, p.div_bu);
+        u = w - bundle * BU;
     }
     TileCoord t;
-    t.qt = p.nq - 1 - u / (G * R);
-    const int g = bundle * G + (u / R) % G;
-    const int r = u % R;
-    t.b = g / p.Hkv;
-    t.hq = (g % p.Hkv) * R + r;
+    t.qt = p.nq - 1 - (int)fdiv(u, p.div_gr);
+    const uint32_t ur = fdiv(u, p.div_r);
+    const uint32_t g = bundle * G + (ur & (G - 1));
+    const uint32_t r = u - ur * R;
+    const uint32_t b = fdiv(g, p.div_hkv);
+    t.b = b;
+    t.kvh = g - b * p.Hkv;
+    t.hq = t.kvh * R + r;
     return t;
 }
 
@@ -162,7 +169,7 @@ void attn_fwd_16(AttnParams p) {
     const int h = lane >> 5;     // half-wave
 
     const TileCoord tc = map_tile(p, blockIdx.x);
-    const int kvh = tc.hq / (p.Hq / p.Hkv);
+    const int kvh = tc.kvh;
     const int off = p.Sk - p.Sq;
     const int qs = tc.qt * BM16;                 // first query of the workgroup
     const int qw = qs + wave * QPW;              // first query of this wave
@@ -490,12 +497,23 @@ void attn_fwd_16(AttnParams p) {
             }
         constexpr int LPR = T::ROW / 16;          // lanes per row
         constexpr int RPS = 64 / LPR;             // rows per store instruction
+        if (qw + QPW <= p.Sq) {
+            // every row of the wave exists: all staging reads first, then the stores
+            u32x4 v[QPW / RPS];
 #pragma unroll
-        for (int i = 0; i < QPW / RPS; ++i) {
-            const int row = RPS * i + lane / LPR;
-            const u32x4 v = *(const u32x4*)(stg + row * SPITCH + 16 * (lane % LPR));
-            if (qw + row < p.Sq)
-                *(u32x4*)((uint8_t*)Og + (int64_t)(qw + row) * T::ROW + 16 * (lane % LPR)) = v;
+            for (int i = 0; i < QPW / RPS; ++i)
+                v[i] = *(const u32x4*)(stg + (RPS * i + lane / LPR) * SPITCH + 16 * (lane % LPR));
+#pragma unroll
+            for (int i = 0; i < QPW / RPS; ++i)
+                *(u32x4*)((uint8_t*)Og + (int64_t)(qw + RPS * i + lane / LPR) * T::ROW + 16 * (lane % LPR)) = v[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < QPW / RPS; ++i) {
+                const int row = RPS * i + lane / LPR;
+                const u32x4 v = *(const u32x4*)(stg + row * SPITCH + 16 * (lane % LPR));
+                if (qw + row < p.Sq)
+                    *(u32x4*)((uint8_t*)Og + (int64_t)(qw + row) * T::ROW + 16 * (lane % LPR)) = v;
+            }
         }
         if (p.lse && h == 0 && qi < p.Sq) {
             const float lse = (le > 0.f) ? (m_run + __log2f(le)) * 0.69314718055994531f : NEG_INF;
@@ -525,7 +543,7 @@ __global__ __launch_bounds__(256) void attn_fwd_32(AttnParams p) {
     const int h = lane >> 5;
 
     const TileCoord tc = map_tile(p, blockIdx.x);
-    const int kvh = tc.hq / (p.Hq / p.Hkv);
+    const int kvh = tc.kvh;
     const int off = p.Sk - p.Sq;
     const int qs = tc.qt * BM32;
     const int qw = qs + wave * 32;
