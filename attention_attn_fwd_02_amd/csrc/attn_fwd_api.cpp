@@ -181,7 +181,9 @@ extern "C" int attn_fwd_rope(const void* q, const void* k, const void* v, void* 
     // the attention kernel addresses the tables with 32-bit byte offsets
     if ((int64_t)Sk * (D / 2) * 4 > (INT64_C(1) << 31) - (INT64_C(1) << 20)) return ATTN_ERR_UNSUPPORTED;
 
-    const void* rk = select_rope(dtype, D, rope_layout);
+    // heads per thread of the key pass: the largest of 4, 2, 1 dividing Hkv
+    const int hb = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0) ? 2 : 1;
+    const void* rk = select_rope(dtype, D, rope_layout, hb);
     if (!rk) return ATTN_ERR_UNSUPPORTED;
     // the attention launch is fully decided (scale, kernel, grid) before the key
     // pass is enqueued, so an error leaves k_rot and every output untouched
@@ -196,7 +198,7 @@ extern "C" int attn_fwd_rope(const void* q, const void* k, const void* v, void* 
     rp.rsin = rope_sin;
     rp.rows = (int64_t)B * Hkv * Sk;
     rp.S = Sk;
-    const int64_t threads = rp.rows * (D / 16);
+    const int64_t threads = rp.rows / hb * (D / 16);
     const int64_t nblk = (threads + 255) / 256;
     if (nblk > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
     void* a1[] = {&rp};

@@ -50,7 +50,7 @@ struct RopeParams {
     int64_t rows;       // B * H * S
     int S;              // row r sits at position r % S
 };
-const void* select_rope(int dtype, int D, int layout);
+const void* select_rope(int dtype, int D, int layout, int hb);
 
 struct KernelChoice {
     const void* fn;   // __global__ function, or null when the combination is unsupported

@@ -49,6 +49,8 @@ SHAPES = [
     ("bf16", 1, 2, 2, 1000, 1000, 64, True, ATTN_ROPE_INTERLEAVED),
     ("fp16", 1, 2, 1, 700, 700, 128, True, ATTN_ROPE_HALVES),
     ("bf16", 1, 6, 2, 300, 300, 128, True, ATTN_ROPE_HALVES),
+    ("bf16", 2, 8, 4, 200, 300, 128, True, ATTN_ROPE_INTERLEAVED),   # key pass: 4 heads per thread
+    ("fp16", 1, 6, 3, 150, 150, 64, False, ATTN_ROPE_HALVES),        # key pass: 1 head per thread
 ]
 
 
