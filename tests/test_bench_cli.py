@@ -1,4 +1,5 @@
-"""bench.py's host logic (CPU): the one-GPU guard and the source-keyed traffic lookup."""
+"""bench.py's host logic (CPU): the one-GPU guard, the source-keyed traffic lookup, the
+clock summary over the timed interval and the window split of the timed steps."""
 import os
 import subprocess
 import sys
@@ -31,3 +32,52 @@ def test_traffic_is_null_for_another_kernel_source(tmp_path):
 
 def test_traffic_is_null_without_a_summary():
     assert bench.committed_traffic("no_such_workload") is None
+
+
+def test_clock_summary_keeps_the_timed_interval():
+    s = bench.SclkSampler()
+    # samples before, inside and after a timed interval [10, 20] (perf_counter seconds)
+    s.values = [(5.0, 2400.0), (11.0, 1900.0), (15.0, 1880.0), (19.0, 1920.0), (25.0, 2400.0)]
+    got = s.summary(10.0, 20.0)
+    assert got["samples"] == 3
+    assert got["median_mhz"] == 1900.0 and got["min_mhz"] == 1880.0 and got["max_mhz"] == 1920.0
+    # no sample inside a short interval: every sample is reported instead of none
+    assert s.summary(12.0, 13.0)["samples"] == 5
+
+
+def test_timed_windows_cover_exactly_the_requested_steps():
+    class Ev:
+        t = 0.0
+
+        def __init__(self, enable_timing=True):
+            self.at = None
+
+        def record(self, stream):
+            self.at = Ev.t
+
+        def elapsed_time(self, other):
+            return other.at - self.at
+
+    class Cuda:
+        Event = Ev
+
+        @staticmethod
+        def synchronize():
+            pass
+
+    class Torch:
+        cuda = Cuda
+
+    calls = []
+
+    def step():
+        calls.append(1)
+        Ev.t += 2.0                      # every step takes 2 ms of "device time"
+
+    for steps in (1, 3, 5, 7, 20):
+        calls.clear()
+        wall, per_launch, wins, (t0, t1) = bench.timed_run(step, steps, None, Torch)
+        assert len(calls) == steps
+        assert len(wins) == min(5, steps)
+        assert abs(per_launch - 2.0) < 1e-9 and all(abs(w - 2.0) < 1e-9 for w in wins)
+        assert t1 >= t0
