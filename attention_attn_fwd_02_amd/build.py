@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_fwd.so")
-SOURCES = [os.path.join(CSRC, "attn_fwd_kernels.hip"), os.path.join(CSRC, "attn_decode_kernels.hip"),
+SOURCES = [os.path.join(CSRC, "attn_fwd_kernels.hip"), os.path.join(CSRC, "attn_fwd32_kernels.hip"),
+           os.path.join(CSRC, "attn_decode_kernels.hip"),
            os.path.join(CSRC, "attn_bwd_kernels.hip"), os.path.join(CSRC, "attn_rope_kernels.hip"),
            os.path.join(CSRC, "attn_fwd_api.cpp")]
 ARCH = "gfx950"

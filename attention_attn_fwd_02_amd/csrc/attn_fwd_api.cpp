@@ -102,7 +102,7 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
                 int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
                 int dtype, int rope, const float* rcos, const float* rsin, FwdLaunch* out) {
     using namespace attn_impl;
-    const KernelChoice kc = select_kernel(dtype, D, causal ? 1 : 0, rope);
+    const KernelChoice kc = select_kernel(dtype, D, causal ? 1 : 0, rope, (int64_t)B * Hq, Sq);
     if (!kc.fn) return ATTN_ERR_UNSUPPORTED;
 
     AttnParams& p = out->p;

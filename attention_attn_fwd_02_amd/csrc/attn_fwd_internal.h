@@ -60,7 +60,11 @@ struct KernelChoice {
 
 // rope: 0 none, 1 interleaved pairs (2i, 2i+1), 2 split halves (i, i + D/2); the
 // rotary variants exist for the 16-bit types only
-KernelChoice select_kernel(int dtype, int D, int causal, int rope = 0);
+// heads = B * Hq; with Sq it decides the fp32 variant (keys split between the waves of
+// a 32-query workgroup when 128-query workgroups would be fewer than the CUs)
+KernelChoice select_kernel(int dtype, int D, int causal, int rope, int64_t heads, int Sq);
+// the fp32 part of select_kernel (attn_fwd32_kernels.hip)
+KernelChoice select_kernel32(int D, int causal, int64_t heads, int Sq);
 
 // Split-KV pass for few query rows: one wave per (batch, K/V head, chunk).
 struct DecodeParams {

@@ -43,47 +43,9 @@
 
 #include "attn_fwd_internal.h"
 #include "attn_kernel_common.h"
+#include "attn_fwd_tile_map.h"
 
 namespace attn_impl {
-
-// Workgroup -> (batch, query head, query tile).  Workgroups are taken in "bundles"
-// of p.gbundle consecutive key/value-head groups; inside a bundle the order is
-// query tile first (heaviest causal tiles of every head in the bundle before any
-// lighter one), then group, then query head.  A bundle is sized (on the host) to
-// fill the workgroup slots of an XCD, which keeps the causal tail balanced while
-// the K/V heads in flight stay few enough for one XCD's L2.  When the groups split
-// evenly over the 8 XCDs (workgroup w is dispatched to XCD w % 8), each XCD gets
-// whole bundles, so every query tile and query head that reads one K/V head runs
-// on the XCD that caches it.
-struct TileCoord { int b, hq, kvh, qt; };
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-    return (uint32_t)(((uint64_t)n * f.m) >> f.s);
-}
-__device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
-    const uint32_t R = p.R;              // query heads per key/value head
-    const uint32_t G = p.gbundle;        // key/value-head groups per bundle
-    const uint32_t BU = G * R * p.nq;    // workgroups per bundle
-    uint32_t bundle, u;
-    if (p.xcd_remap) {
-        const uint32_t xcd = w & 7, slot = (uint32_t)w >> 3;
-        const uint32_t k = fdiv(slot, p.div_bu);
-        bundle = xcd + 8 * k;
-        u = slot - k * BU;
-    } else {
-        bundle = fdiv(w, p.div_bu);
-        u = w - bundle * BU;
-    }
-    TileCoord t;
-    t.qt = p.nq - 1 - (int)fdiv(u, p.div_gr);
-    const uint32_t ur = fdiv(u, p.div_r);
-    const uint32_t g = bundle * G + (ur & (G - 1));
-    const uint32_t r = u - ur * R;
-    const uint32_t b = fdiv(g, p.div_hkv);
-    t.b = b;
-    t.kvh = g - b * p.Hkv;
-    t.hq = t.kvh * R + r;
-    return t;
-}
 
 // ---------------------------------------------------------------------------
 // 16-bit kernel
@@ -523,164 +485,6 @@ void attn_fwd_16(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel: v_mfma_f32_32x32x2_f32, 4 waves x 32 queries, 32-key tiles.
-// ---------------------------------------------------------------------------
-constexpr int BM32 = 128;
-constexpr int BN32 = 32;
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_32(AttnParams p) {
-    constexpr int KP = D + 1;       // row pitch (floats) of the K and V tiles
-    constexpr int KSTEPS = D / 2;
-    constexpr int DBLK = D / 32;
-    __shared__ float ks[BN32 * KP];
-    __shared__ float vs[BN32 * KP];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int n = lane & 31;
-    const int h = lane >> 5;
-
-    const TileCoord tc = map_tile(p, blockIdx.x);
-    const int kvh = tc.kvh;
-    const int off = p.Sk - p.Sq;
-    const int qs = tc.qt * BM32;
-    const int qw = qs + wave * 32;
-
-    const float* __restrict__ Qg = (const float*)p.q + ((int64_t)(tc.b * p.Hq + tc.hq) * p.Sq) * D;
-    const float* __restrict__ Kg = (const float*)p.k + ((int64_t)(tc.b * p.Hkv + kvh) * p.Sk) * D;
-    const float* __restrict__ Vg = (const float*)p.v + ((int64_t)(tc.b * p.Hkv + kvh) * p.Sk) * D;
-    float* __restrict__ Og = (float*)p.o + ((int64_t)(tc.b * p.Hq + tc.hq) * p.Sq) * D;
-
-    const int last_q = min(qs + BM32, p.Sq) - 1;
-    int kend = p.Sk;
-    if (CAUSAL) kend = min(p.Sk, last_q + off + 1);
-    const int ntiles = kend > 0 ? (kend + BN32 - 1) / BN32 : 0;
-    const int wlast_q = min(qw + 32, p.Sq) - 1;
-    int wkend = (qw < p.Sq) ? p.Sk : 0;
-    if (CAUSAL && qw < p.Sq) wkend = min(p.Sk, wlast_q + off + 1);
-
-    // Q^T fragments: lane (n, h) holds Q[qw + n][2s + h]
-    float qf[KSTEPS];
-    {
-        const int qrow = qw + n;
-        const float sgn = (p.q_mode == 1) ? -1.f : 1.f;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            float x = 0.f;
-            if (qrow < p.Sq && p.q_mode != 2) x = Qg[(int64_t)qrow * D + 2 * s + h] * sgn;
-            qf[s] = x;
-        }
-    }
-    f32x16 oacc[DBLK];
-#pragma unroll
-    for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
-    float m_run = NEG_INF, l_run = 0.f;
-
-    // K and V tiles go through registers: the next tile's 16-byte loads are issued
-    // before the current tile is computed, so their latency overlaps the MFMAs
-    constexpr int NPF = BN32 * D / 4 / 256;        // float4 per thread per tile and tensor
-    // (rows past Sk, and the tile after the last, are clamped to row 0 and zeroed)
-    float4 kpre[NPF], vpre[NPF];
-#define ATTN32_LOAD_TILE(J)                                                               \
-    _Pragma("unroll") for (int i = 0; i < NPF; ++i) {                                     \
-        const int e = 4 * (tid + 256 * i);                                                \
-        const int row = e / D, col = e % D;                                               \
-        const bool ok = (J) < ntiles && (J) * BN32 + row < p.Sk;                          \
-        const int64_t off32 = ok ? (int64_t)((J) * BN32 + row) * D + col : (int64_t)col;  \
-        const float4 kx = *(const float4*)(Kg + off32);                                   \
-        const float4 vx = *(const float4*)(Vg + off32);                                   \
-        kpre[i] = ok ? kx : make_float4(0.f, 0.f, 0.f, 0.f);                              \
-        vpre[i] = ok ? vx : make_float4(0.f, 0.f, 0.f, 0.f);                              \
-    }
-    ATTN32_LOAD_TILE(0)
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = j * BN32;
-        __syncthreads();     // previous tile fully consumed
-#pragma unroll
-        for (int i = 0; i < NPF; ++i) {
-            const int e = 4 * (tid + 256 * i);
-            const int row = e / D, col = e % D;
-            float* kd = ks + row * KP + col;
-            float* vd = vs + row * KP + col;
-            kd[0] = kpre[i].x; kd[1] = kpre[i].y; kd[2] = kpre[i].z; kd[3] = kpre[i].w;
-            vd[0] = vpre[i].x; vd[1] = vpre[i].y; vd[2] = vpre[i].z; vd[3] = vpre[i].w;
-        }
-        __syncthreads();
-        ATTN32_LOAD_TILE(j + 1)
-        if (k0 >= wkend) continue;
-
-        f32x16 sacc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[n * KP + 2 * s + h], qf[s], sacc, 0, 0, 0);
-
-        const bool need_mask = (k0 + BN32 > p.Sk) || (CAUSAL && (k0 + BN32 - 1 > qw + off));
-        if (need_mask) {
-            const int qi = qw + n;
-            const int lim = CAUSAL ? min(p.Sk - 1, qi + off) : (p.Sk - 1);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (key > lim) sacc[r] = NEG_INF;
-            }
-        }
-        float mx = NEG_INF;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m_run, mx * p.c);
-        const bool empty = (m_new == NEG_INF);
-        const float m_use = empty ? 0.f : m_new;
-        const float alpha = empty ? 1.f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            sacc[r] = fast_exp2(fmaf(sacc[r], p.c, -m_use));
-            rs += sacc[r];
-        }
-        l_run = l_run * alpha + rs;
-#pragma unroll
-        for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-        // O^T += V^T . P^T: step r pairs accumulator register r (key 8(r/4) + 4h + r%4)
-        // with the V row of the same key
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-#pragma unroll
-            for (int d = 0; d < DBLK; ++d)
-                oacc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * KP + 32 * d + n], sacc[r],
-                                                                oacc[d], 0, 0, 0);
-        }
-    }
-
-    const int qi = qw + n;
-    const float l_tot = pair_sum(l_run);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    if (qi < p.Sq) {
-        float* orow = Og + (int64_t)qi * D;
-#pragma unroll
-        for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) orow[32 * d + 8 * (r >> 2) + 4 * h + (r & 3)] = oacc[d][r] * inv;
-        if (p.lse && h == 0) {
-            const float lse = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : NEG_INF;
-            p.lse[(int64_t)(tc.b * p.Hq + tc.hq) * p.Sq + qi] = lse;
-        }
-    }
-}
-
-#undef ATTN32_LOAD_TILE
-
-// ---------------------------------------------------------------------------
 // kernel selection
 // ---------------------------------------------------------------------------
 template <int DT, int D, int ROPE>
@@ -692,19 +496,12 @@ static const void* pick16(int causal, int rope) {
     return rope == 0 ? pick16r<DT, D, 0>(causal) : rope == 1 ? pick16r<DT, D, 1>(causal)
          : rope == 2 ? pick16r<DT, D, 2>(causal) : nullptr;
 }
-template <int D>
-static const void* pick32(int causal) {
-    return causal ? (const void*)&attn_fwd_32<D, true> : (const void*)&attn_fwd_32<D, false>;
-}
 
-KernelChoice select_kernel(int dtype, int D, int causal, int rope) {
+KernelChoice select_kernel(int dtype, int D, int causal, int rope, int64_t heads, int Sq) {
     KernelChoice kc = {nullptr, 0, 0};
     if (dtype == ATTN_IMPL_FP32) {
         if (rope != 0) return kc;
-        kc.bm = BM32;
-        kc.threads = 256;
-        kc.fn = (D == 64) ? pick32<64>(causal) : (D == 128) ? pick32<128>(causal) : nullptr;
-        return kc;
+        return select_kernel32(D, causal, heads, Sq);
     }
     kc.bm = BM16;
     kc.threads = 64 * NW;

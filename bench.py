@@ -49,7 +49,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 CSRC = os.path.join(ROOT, "attention_attn_fwd_02_amd", "csrc")
-KERNEL_SRC = os.path.join(CSRC, "attn_fwd_kernels.hip")
+# the sources whose hash a forward traffic summary carries: the kernels and their tile map
+KERNEL_SRC = (os.path.join(CSRC, "attn_fwd_kernels.hip"), os.path.join(CSRC, "attn_fwd_tile_map.h"))
 PROFILES = os.path.join(ROOT, "profiles")
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # dense MFMA peaks, MI355X
 HBM_PEAK_GBS = 8000.0                                             # HBM3E, MI355X
@@ -59,9 +60,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(src: str = KERNEL_SRC) -> str:
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(src=KERNEL_SRC) -> str:
+    """First 16 hex digits of the SHA-256 of one source file, or of several read one
+    after the other."""
+    h = hashlib.sha256()
+    for path in ((src,) if isinstance(src, str) else src):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic(workload: str, prefix: str = "attn_fwd", src: str = KERNEL_SRC):

@@ -25,9 +25,16 @@ def test_traffic_is_read_for_the_current_kernel_source():
 
 def test_traffic_is_null_for_another_kernel_source(tmp_path):
     src = tmp_path / "changed.hip"
-    with open(bench.KERNEL_SRC, "rb") as f:
+    with open(bench.KERNEL_SRC[0], "rb") as f:
         src.write_bytes(f.read() + b"\n// changed\n")
-    assert bench.committed_traffic("mha_causal_bf16_b2_h32_s4096_d128", src=str(src)) is None
+    assert bench.committed_traffic("mha_causal_bf16_b2_h32_s4096_d128",
+                                   src=(str(src), bench.KERNEL_SRC[1])) is None
+    # a change to the tile map header alone is a different kernel too
+    hdr = tmp_path / "changed.h"
+    with open(bench.KERNEL_SRC[1], "rb") as f:
+        hdr.write_bytes(f.read() + b"\n// changed\n")
+    assert bench.committed_traffic("mha_causal_bf16_b2_h32_s4096_d128",
+                                   src=(bench.KERNEL_SRC[0], str(hdr))) is None
 
 
 def test_traffic_is_null_without_a_summary():

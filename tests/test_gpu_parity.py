@@ -39,6 +39,9 @@ SHAPES = [
     ("fp32", 1, 2, 2, 300, 300, 128, True),
     ("fp32", 1, 4, 2, 131, 77, 64, True),
     ("fp32", 2, 4, 1, 70, 190, 128, False),
+    ("fp32", 1, 2, 1, 200, 333, 64, True),       # keys split between waves, more keys than queries
+    ("fp32", 1, 2, 2, 300, 100, 128, True),      # keys split between waves, empty rows
+    ("fp32", 2, 32, 8, 512, 512, 64, True),      # 256 tiles of 128 queries: one wave per query block
 ]
 
 
