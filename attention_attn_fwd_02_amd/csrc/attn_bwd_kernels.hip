@@ -85,7 +85,8 @@ __device__ __forceinline__ void dma_part(__amdgpu_buffer_rsrc_t rs, uint8_t* dst
 
 // Stage a wave's 32 x D fp32 result (lane = output row, registers = 4-runs of
 // columns, the layout of an MFMA accumulator with rows on lanes) through its LDS
-// region and store rows [row0, row0 + 32) below `nrows` as 16-bit values.
+// region and store rows [row0, row0 + 32) below `nrows` as 16-bit values, with the
+// non-temporal hint (gradients are not read again by the launch).
 template <int DT, int D>
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mul, uint8_t* stg,
                                            uint8_t* out, int64_t row0, int nrows, int lane) {
@@ -109,7 +110,7 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mu
         const int row = RPS * i + lane / LPR;
         const u32x4 v = *(const u32x4*)(stg + row * SPITCH + 16 * (lane % LPR));
         if (row < nrows)
-            *(u32x4*)(out + (row0 + row) * ROW + 16 * (lane % LPR)) = v;
+            __builtin_nontemporal_store(v, (u32x4*)(out + (row0 + row) * ROW + 16 * (lane % LPR)));
     }
 }
 
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce(BwdParams p) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = E::pack(a[2 * e] * mul, a[2 * e + 1] * mul);
-        *(u32x4*)((uint8_t*)(t == 0 ? p.dk : p.dv) + 2 * i) = w;
+        __builtin_nontemporal_store(w, (u32x4*)((uint8_t*)(t == 0 ? p.dk : p.dv) + 2 * i));
     }
 }
 

@@ -441,7 +441,9 @@ void attn_fwd_16(AttnParams p) {
 
     // ---- epilogue: O = O^T / le, rounded once; LSE = ln2 * (m + log2 le).  The
     // wave stages its 32 output rows in a private LDS tile (rows padded by 16 bytes)
-    // and stores them row-contiguously, 16 bytes per lane.
+    // and stores them row-contiguously, 16 bytes per lane, with the non-temporal
+    // hint (the output is not read again by this launch, and the lines leave the
+    // cache as they are written instead of all at the end of the launch).
     {
         const int qi = qw + n;
         const float le = pair_sum(le_run);
@@ -467,14 +469,15 @@ void attn_fwd_16(AttnParams p) {
                 v[i] = *(const u32x4*)(stg + (RPS * i + lane / LPR) * SPITCH + 16 * (lane % LPR));
 #pragma unroll
             for (int i = 0; i < QPW / RPS; ++i)
-                *(u32x4*)((uint8_t*)Og + (int64_t)(qw + RPS * i + lane / LPR) * T::ROW + 16 * (lane % LPR)) = v[i];
+                __builtin_nontemporal_store(
+                    v[i], (u32x4*)((uint8_t*)Og + (int64_t)(qw + RPS * i + lane / LPR) * T::ROW + 16 * (lane % LPR)));
         } else {
 #pragma unroll
             for (int i = 0; i < QPW / RPS; ++i) {
                 const int row = RPS * i + lane / LPR;
                 const u32x4 v = *(const u32x4*)(stg + row * SPITCH + 16 * (lane % LPR));
                 if (qw + row < p.Sq)
-                    *(u32x4*)((uint8_t*)Og + (int64_t)(qw + row) * T::ROW + 16 * (lane % LPR)) = v;
+                    __builtin_nontemporal_store(v, (u32x4*)((uint8_t*)Og + (int64_t)(qw + row) * T::ROW + 16 * (lane % LPR)));
             }
         }
         if (p.lse && h == 0 && qi < p.Sq) {
