@@ -1,8 +1,9 @@
 """Parity of the HIP path with the fp64 oracle, element by element (GPU).
 
 Small and ragged shapes, the five named workloads and the attention variants
-at full size compare every output element (O and LSE); the million-key case
-compares sampled rows the oracle computes one by one."""
+at full size compare every output element (O and LSE); the million-key case and
+the largest head slice the library accepts (8,384,512 keys of 256 bytes) compare
+sampled rows the oracle computes one by one."""
 import zlib
 
 import numpy as np
@@ -133,3 +134,42 @@ def test_long_context_large_offsets():
     o_ref1, lse_ref1 = oracle.attn_fwd(q, k, v, causal=True, rows=last)
     e1 = compare(o1.reshape(-1, w.D).cpu(), l1.reshape(-1).cpu(), o_ref1, lse_ref1, "bf16", w.name)
     say("  decode, last rows: max|dO| %.3g  max|dLSE| %.3g" % e1)
+
+
+@pytest.mark.parametrize("dtype,D,Sk", [
+    ("bf16", 128, ((1 << 31) - (1 << 20)) // 256),    # 8,384,512 keys: K and V 2 GiB - 1 MiB each
+    ("fp32", 64, ((1 << 31) - (1 << 20)) // 256),     # the fp32 kernels at the same byte limit
+])
+def test_largest_head_slice(dtype, D, Sk):
+    """The largest K/V head slice the library accepts (2^31 - 2^20 bytes, byte
+    offsets up to just below 2^31 inside a head, the out-of-range DMA offsets
+    summed with tile offsets near 2^31 without wrapping): causal prefill with the
+    queries at the end of the keys, on sampled rows, and split-KV decoding of the
+    last row (bf16), against the oracle."""
+    from attention_attn_fwd_02_amd import fwd, fwd_decode
+    from attention_attn_fwd_02_amd.attn import ATTN_ERR_UNSUPPORTED, AttnError
+    w = W.custom(dtype, 1, 1, 1, 130, Sk, D, True, seed=777 + D)
+    say("case", w.name)
+    q, k, v = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o, lse = fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 65, 127, 128, 129] + [3, 40, 77, 100, 111, 120, 125, 126])
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=True, rows=rows)
+    og = o.reshape(-1, w.D)[torch.from_numpy(rows)].cpu()
+    lg = lse.reshape(-1)[torch.from_numpy(rows)].cpu()
+    e = compare(og, lg, o_ref, lse_ref, dtype, w.name)
+    say("  prefill, %d rows: max|dO| %.3g  max|dLSE| %.3g" % ((len(rows),) + e))
+    if dtype != "fp32":
+        o1, l1 = fwd_decode(qd[:, :, -1:].contiguous(), kd, vd, causal=True)
+        torch.cuda.synchronize()
+        last = int(np.flatnonzero(rows == w.Sq - 1)[0])      # the oracle's row of query Sq - 1
+        e1 = compare(o1.reshape(-1, w.D).cpu(), l1.reshape(-1).cpu(), o_ref[last:last + 1],
+                     lse_ref[last:last + 1], dtype, w.name)
+        say("  decode, last row: max|dO| %.3g  max|dLSE| %.3g" % e1)
+    # one more key and the head slice no longer fits: refused before any launch
+    k1 = torch.empty((1, 1, Sk + 1, D), dtype=kd.dtype, device=dev)
+    with pytest.raises(AttnError) as ei:
+        fwd(qd, k1, k1, causal=True)
+    assert ei.value.status == ATTN_ERR_UNSUPPORTED
