@@ -33,8 +33,8 @@
 //     units work on independent data;
 //   * the softmax reference m is raised only when needed (first visible keys, or
 //     a block whose weights sum past 2^8), so the common path has no max pass.
-// fp32 path: the same dataflow with v_mfma_f32_32x32x2_f32 (true fp32 products),
-// 32 queries per wave, 32-key tiles in LDS, the next tile prefetched into registers.
+// fp32 inputs run the kernels of attn_fwd32_kernels.hip (the same dataflow with true
+// fp32 products); select_kernel below hands them over.
 //
 // The mask, the grouped-head mapping and the empty-row convention are those of
 // include/attn_fwd.h.
