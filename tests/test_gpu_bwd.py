@@ -16,24 +16,9 @@ import torch
 import oracle
 from attention_attn_fwd_02_amd import bwd, fwd
 from attention_attn_fwd_02_amd import workloads as W
-from gpu_helpers import say
+from gpu_helpers import bwd_tolerance, say
 
 pytestmark = pytest.mark.gpu
-
-
-def bwd_tolerance(ref, dtype):
-    """Max-abs bound for one gradient tensor: a relative error of 2^-6 of the
-    tensor's largest magnitude, and never less than 4e-3 absolute.
-
-    Reasoning: the inputs are exact; the GPU rounds P and dS to the 16-bit type
-    before they multiply (relative 2^-9 each for bf16, 2^-12 for fp16) and uses the
-    forward's O rounded to the 16-bit type in D = dO.O; each gradient element sums
-    up to Sk (or Sq) such rounded products whose signs vary, so the accumulated
-    relative error stays a small multiple of 2^-9 of the largest terms, and the
-    output rounding adds 2^-9 of the element.  2^-6 leaves a factor of eight for the
-    summation; the absolute floor covers elements that cancel to near zero."""
-    m = float(np.abs(ref).max()) if ref.size else 0.0
-    return max(2.0 ** -6 * m, 4e-3)
 
 
 def run_bwd(w, seed_g, scale=None):
