@@ -35,6 +35,10 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError("libattn_fwd.so is not built (%s); run "
                            "`python -m attention_attn_fwd_02_amd.build`" % path)
+    # torch ships its own HIP runtime under another file name; loaded first, it also
+    # serves this library (same soname).  Loaded after this library, it would be a
+    # second runtime, whose streams and memory this library's kernels cannot use.
+    import torch  # noqa: F401  (no GPU access: importing does not initialise a device)
     lib = ctypes.CDLL(path)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
