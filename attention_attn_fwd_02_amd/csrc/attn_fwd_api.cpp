@@ -6,6 +6,7 @@
 
 #include "attn_fwd.h"
 #include "attn_fwd_internal.h"
+#include "attn_fwd_tile_map.h"
 
 namespace {
 
@@ -79,13 +80,6 @@ size_t decode_workspace(int64_t rows, int D, int nsplit) {
 }
 
 // Multiplier and shift of the division by d (1 <= d < 2^31) for dividends below 2^31.
-attn_impl::FastDiv make_fastdiv(uint32_t d) {
-    uint32_t l = 0;
-    while (l < 31 && (1u << l) < d) ++l;                 // l = ceil(log2 d)
-    const uint32_t s = 31 + l;
-    const uint64_t m = (((uint64_t)1 << s) + d - 1) / d;  // ceil(2^s / d) < 2^32
-    return attn_impl::FastDiv{(uint32_t)m, s};
-}
 
 // Everything one prefill launch needs, decided on the host before anything is enqueued.
 struct FwdLaunch {
@@ -126,18 +120,7 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
     const int64_t per_group = (int64_t)(Hq / Hkv) * p.nq;
     const int64_t nwg = groups * per_group;
     if (nwg > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
-    // Bundle key/value-head groups until a bundle holds at least 64 workgroups (two
-    // rounds of an XCD's 32 CUs), heaviest query tiles of the whole bundle first;
-    // the bundle count must divide the groups (and split over the 8 XCDs to remap).
-    int gb = 1;
-    while (gb * per_group < 64 && groups % (2 * gb) == 0) gb *= 2;
-    p.gbundle = gb;
-    p.xcd_remap = ((groups / gb) % 8 == 0) ? 1 : 0;
-    p.R = Hq / Hkv;
-    p.div_bu = make_fastdiv((uint32_t)((int64_t)gb * per_group));
-    p.div_gr = make_fastdiv((uint32_t)(gb * p.R));
-    p.div_r = make_fastdiv((uint32_t)p.R);
-    p.div_hkv = make_fastdiv((uint32_t)Hkv);
+    plan_tile_map(p, groups, per_group, Hq / Hkv);
     out->fn = kc.fn;
     out->nwg = (unsigned)nwg;
     out->threads = kc.threads;

@@ -1,5 +1,7 @@
 // attn_fwd_tile_map.h -- the prefill kernels' workgroup -> tile mapping (16-bit and
-// fp32 kernels).  Included by the .hip sources only.
+// fp32 kernels): the host plans it (plan_tile_map), every workgroup decodes its own
+// tile (map_tile).  Both sides are plain inline code, so the host test of the mapping
+// runs the same functions the kernels do.
 #ifndef ATTN_FWD_TILE_MAP_H
 #define ATTN_FWD_TILE_MAP_H
 
@@ -20,10 +22,10 @@ namespace attn_impl {
 // whole bundles, so every query tile and query head that reads one K/V head runs
 // on the XCD that caches it.
 struct TileCoord { int b, hq, kvh, qt; };
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
     return (uint32_t)(((uint64_t)n * f.m) >> f.s);
 }
-__device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
+__host__ __device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
     const uint32_t R = p.R;              // query heads per key/value head
     const uint32_t G = p.gbundle;        // key/value-head groups per bundle
     const uint32_t BU = G * R * p.nq;    // workgroups per bundle
@@ -47,6 +49,32 @@ __device__ __forceinline__ TileCoord map_tile(const AttnParams& p, int w) {
     t.kvh = g - b * p.Hkv;
     t.hq = t.kvh * R + r;
     return t;
+}
+
+// The multiplier and shift of FastDiv for a divisor d >= 1 (host).
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while (l < 31 && (1u << l) < d) ++l;                 // l = ceil(log2 d)
+    const uint32_t s = 31 + l;
+    const uint64_t m = (((uint64_t)1 << s) + d - 1) / d;  // ceil(2^s / d) < 2^32
+    return FastDiv{(uint32_t)m, s};
+}
+
+// Host side of the mapping for `groups` key/value-head groups (B * Hkv) of `per_group`
+// workgroups each (R * nq): bundle groups until a bundle holds at least 64 workgroups
+// (two rounds of an XCD's 32 CUs), heaviest query tiles of the whole bundle first; the
+// bundle count must divide the groups, and whole bundles go to each XCD when the
+// bundles split evenly over the 8 XCDs.  Needs p.Hkv, p.nq and R = Hq / Hkv.
+inline void plan_tile_map(AttnParams& p, int64_t groups, int64_t per_group, int R) {
+    int gb = 1;
+    while (gb * per_group < 64 && groups % (2 * gb) == 0) gb *= 2;
+    p.gbundle = gb;
+    p.xcd_remap = ((groups / gb) % 8 == 0) ? 1 : 0;
+    p.R = R;
+    p.div_bu = make_fastdiv((uint32_t)((int64_t)gb * per_group));
+    p.div_gr = make_fastdiv((uint32_t)(gb * R));
+    p.div_r = make_fastdiv((uint32_t)R);
+    p.div_hkv = make_fastdiv((uint32_t)p.Hkv);
 }
 
 }  // namespace attn_impl
