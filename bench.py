@@ -268,15 +268,21 @@ def decode_line(args, w, name, wall_ms, kern_ms, med_ms, clock):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--gpus", type=int, default=1,
+                    help="GPUs to run on; only 1 is supported (the path has no multi-GPU part)")
+    ap.add_argument("--steps", type=int, default=200, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps after the settle phase")
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="untimed clock-settle phase before the warm-up, in seconds of wall time")
-    ap.add_argument("--workload", default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--workload", default=None,
+                    help="a workload of attention_attn_fwd_02_amd/workloads.py (default: the headline, "
+                         "causal bf16 B=2 H=32 S=4096 D=128)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="about how long the oracle's CPU baseline sample runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle's CPU baseline")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many MiB (the "
+                         "reference for scaling the HBM traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
